@@ -1,0 +1,421 @@
+"""Pins of the CPU oracle against facts fixed by the mathematics.
+
+Each ``pin_*`` function takes a loaded oracle library, raises AssertionError
+when the oracle disagrees with the fact it checks, and returns nothing
+otherwise.  They are collected as tests in ``test_oracle_pins.py`` and are
+also run against deliberately broken copies of the oracle in
+``test_oracle_mutants.py`` (every broken copy must fail at least one pin).
+
+The facts:
+
+* P-ENUM -- on tiny vocabularies the whole stochastic step is enumerated
+  exactly (every draft tuple, every decision cell, every sampling cell) from
+  the oracle's own observable behaviour, and the resulting law of emitted
+  tokens must equal the target distribution at every position, conditionally
+  on reaching it.  This is the defining property of lossless speculative
+  verification: the output behaves like sampling the target model
+  (aidevelopers.cz, "Zkoumání spekulativního dekódování v vLLM na AMD GPU",
+  section "Základní autoregresivní dekódování").
+* P-LIB -- special cases that reduce to library routines: probabilities equal
+  float64 softmax; greedy choices equal ``numpy.argmax`` (first maximum);
+  with draft == target every token is accepted and the bonus token is
+  ``numpy.searchsorted(cumsum(p_k), r, 'right')``; with a one-hot draft the
+  residual is the target with that token removed; multi-candidate greedy
+  equals brute force over candidates.
+* Closed forms worked by hand on dyadic probabilities.
+* P-INV -- invariants: 0 <= a <= k, accepted tokens are the draft tokens, the
+  tail is -1, the corrective token lies where p > q, the residual sums to 1.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+from oracle import svo
+
+F32 = svo.F32
+
+
+def softmax64(x, tau=1.0):
+    x = np.asarray(x, np.float64) / tau
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def f32_below(x):
+    """Largest float32 strictly below x (x > 0)."""
+    f = np.float32(x)
+    if float(f) >= x:
+        f = np.nextafter(f, np.float32(0))
+    return f
+
+
+def f32_at_or_above(x):
+    """Smallest float32 >= x."""
+    f = np.float32(x)
+    if float(f) < x:
+        f = np.nextafter(f, np.float32(2))
+    return f
+
+
+def _tile_rows(rows, n):
+    return np.ascontiguousarray(np.broadcast_to(rows, (n,) + rows.shape))
+
+
+# ---------------------------------------------------------------- P-ENUM ----
+
+def exact_emission_law(lib, t, d, tau):
+    """Exact law of the stochastic step for one fixed set of logit rows.
+
+    t: float32 [k+1][V]; d: float32 [k][V].  Draft tokens are drawn from
+    q_i = softmax(d_i/tau) (computed here with numpy).  The oracle is used as a
+    black box plus its own diagnostics, and every diagnostic it is trusted for
+    is checked against its behaviour first:
+      * the acceptance threshold acc_i = min(1, p_i(x_i)/q_i(x_i)) from its px/qx
+        must be where its decision flips (checked at the float32 neighbours);
+      * the sampling cells from svo_emit_cdf must be where its inverse CDF
+        lands (checked at every cell midpoint).
+    Returns (X, W, acc, cellw): draft tuples [N][k], their probabilities [N],
+    acceptance thresholds [N][k], and per-position sampling cell widths
+    [k+1][V] (cellw[a] is the law of the extra token when a is the first
+    rejection, a == k meaning all accepted)."""
+    k, V = d.shape
+    q = softmax64(d, tau)
+    X = np.array(list(itertools.product(range(V), repeat=k)), np.int32).reshape(-1, k)
+    N = X.shape[0]
+    W = np.prod(q[np.arange(k)[None, :], X], axis=1)
+    T = _tile_rows(t.astype(np.float32), N)
+    D = _tile_rows(d.astype(np.float32), N)
+    zeros_u = np.zeros((N, k), np.float32)
+    half_r = np.full(N, 0.5, np.float32)
+
+    # diagnostics with every decision forced to "accept"
+    force = np.full((N, k), svo.FORCE_ACCEPT, np.int8)
+    o = svo.verify_stochastic(T, D, X, zeros_u, half_r, B=N, k=k, V=V,
+                              temperature=tau, force=force, lib=lib)
+    px, qx = o["px"], o["qx"]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rho = np.where(qx > 0, px / np.where(qx > 0, qx, 1.0), np.where(px > 0, np.inf, 0.0))
+    acc = np.minimum(1.0, rho)
+
+    # the decision at position i flips exactly at acc_i
+    for i in range(k):
+        f = np.zeros((N, k), np.int8)
+        f[:, :i] = svo.FORCE_ACCEPT
+        for side in ("below", "above"):
+            u = np.zeros((N, k), np.float32)
+            if side == "below":
+                ok = acc[:, i] > 0
+                u[:, i] = [f32_below(a) if a > 0 else 0.0 for a in acc[:, i]]
+                expect_accept = ok
+            else:
+                ok = acc[:, i] < 1
+                u[:, i] = [f32_at_or_above(a) if a < 1 else np.float32(0.0) for a in acc[:, i]]
+                expect_accept = ~ok
+            r = svo.verify_stochastic(T, D, X, u, half_r, B=N, k=k, V=V, temperature=tau,
+                                      force=f, lib=lib)
+            accepted = r["accept_len"] > i
+            sel = ok
+            assert np.array_equal(accepted[sel], expect_accept[sel]), \
+                f"decision at position {i} does not flip at min(1, p/q) ({side})"
+
+    # sampling cells of the extra token at each possible first-rejection point
+    cellw = np.zeros((k + 1, V))
+    t1, d1 = t.astype(np.float32), d.astype(np.float32)
+    for a in range(k + 1):
+        los, his = [], []
+        for y in range(V):
+            lo, hi = svo.emit_cdf(t1, d1, b=0, k=k, V=V, a=a, y=y, temperature=tau, lib=lib)
+            los.append(lo)
+            his.append(hi)
+        los, his = np.array(los), np.array(his)
+        cellw[a] = his - los
+        # contiguity of the cells and total mass 1
+        assert abs(los[0]) < 1e-15 and abs(his[-1] - 1.0) < 1e-12
+        assert np.allclose(los[1:], his[:-1], rtol=0, atol=1e-15)
+        # the oracle's inverse CDF lands in the cell of every token with room
+        ys = [y for y in range(V) if cellw[a, y] > 1e-6]
+        f = np.zeros((len(ys), k), np.int8)
+        f[:, :a] = svo.FORCE_ACCEPT
+        if a < k:
+            f[:, a] = svo.FORCE_REJECT
+        rr = np.array([np.float32((los[y] + his[y]) / 2) for y in ys], np.float32)
+        xs = np.zeros((len(ys), k), np.int32)
+        res = svo.verify_stochastic(_tile_rows(t1, len(ys)), _tile_rows(d1, len(ys)), xs,
+                                    np.zeros((len(ys), k), np.float32), rr, B=len(ys), k=k,
+                                    V=V, temperature=tau, force=f, lib=lib)
+        assert np.array_equal(res["accept_len"], np.full(len(ys), a))
+        assert np.array_equal(res["tokens"][:, a], np.array(ys)), \
+            f"inverse CDF at position {a} does not follow its cells"
+    return X, W, acc, cellw
+
+
+def check_target_law(t, X, W, acc, cellw, tau, atol=1e-12):
+    """Emission at position j, given it is reached with prefix z, must be p_j."""
+    k = X.shape[1]
+    V = t.shape[1]
+    p = softmax64(t, tau)
+    reach_w = W.copy()  # W(x) * prod_{i<j} acc_i(x)
+    for j in range(k + 1):
+        prefixes = {}
+        for n in range(X.shape[0]):
+            z = tuple(X[n, :j])
+            e = prefixes.setdefault(z, [0.0, np.zeros(V)])
+            e[0] += reach_w[n]
+            if j < k:
+                e[1][X[n, j]] += reach_w[n] * acc[n, j]
+                e[1] += reach_w[n] * (1.0 - acc[n, j]) * cellw[j]
+            else:
+                e[1] += reach_w[n] * cellw[k]
+        for z, (reach, emit) in prefixes.items():
+            assert np.allclose(emit, reach * p[j], rtol=0, atol=atol), \
+                f"position {j}, prefix {z}: emitted law {emit / max(reach, 1e-300)} != target {p[j]}"
+        if j < k:
+            reach_w = reach_w * acc[:, j]
+
+
+def enum_cases():
+    """(t, d, tau) cases for exact enumeration: V <= 8, k <= 3."""
+    rng = np.random.default_rng(20240611)
+    cases = []
+    for (V, k, tau, scale) in [(2, 1, 1.0, 1.0), (3, 2, 1.0, 2.0), (4, 3, 0.7, 1.5),
+                               (5, 2, 1.3, 3.0), (8, 2, 1.0, 1.0), (6, 3, 1.0, 0.5)]:
+        t = (rng.standard_normal((k + 1, V)) * scale).astype(np.float32)
+        d = (t[:k] + rng.standard_normal((k, V)) * scale).astype(np.float32)
+        cases.append((t, d, tau))
+    # draft with -inf entries (q = 0 on some tokens) and target with -inf entries
+    t = np.array([[0.5, -np.inf, 1.0, 0.0], [0.0, 0.3, -1.0, 2.0], [1.0, 1.0, 1.0, -np.inf]],
+                 np.float32)
+    d = np.array([[-np.inf, 0.2, 1.5, 0.1], [0.0, -np.inf, -np.inf, 1.0]], np.float32)
+    cases.append((t, d, 1.0))
+    # draft identical to target at one position (acceptance certain there)
+    t = rng.standard_normal((3, 5)).astype(np.float32)
+    d = np.stack([t[0], rng.standard_normal(5).astype(np.float32)])
+    cases.append((t, d, 0.9))
+    return cases
+
+
+def pin_enumeration(lib):
+    for (t, d, tau) in enum_cases():
+        X, W, acc, cellw = exact_emission_law(lib, t, d, tau)
+        check_target_law(t, X, W, acc, cellw, tau)
+
+
+# ----------------------------------------------------------------- P-LIB ----
+
+def pin_softmax(lib):
+    """p_i(x), q_i(x) equal float64 softmax for every token x."""
+    rng = np.random.default_rng(7)
+    for (V, k, tau, off) in [(7, 2, 1.0, 0.0), (33, 3, 0.7, 0.0), (1000, 1, 1.7, 0.0),
+                             (40, 2, 1.0, 1000.0)]:
+        # off: softmax is shift invariant; logits near 1000 overflow exp()
+        # unless the row maximum is taken out first.
+        t = (rng.standard_normal((k + 1, V)) * 3 + off).astype(np.float32)
+        d = (rng.standard_normal((k, V)) * 3 - off).astype(np.float32)
+        t[0, 3] = -np.inf
+        n = V
+        X = np.tile(np.arange(V, dtype=np.int32)[:, None], (1, k))
+        f = np.full((n, k), svo.FORCE_ACCEPT, np.int8)
+        o = svo.verify_stochastic(_tile_rows(t, n), _tile_rows(d, n), X,
+                                  np.zeros((n, k), np.float32), np.zeros(n, np.float32),
+                                  B=n, k=k, V=V, temperature=tau, force=f, lib=lib)
+        p = softmax64(t, tau)
+        q = softmax64(d, tau)
+        for i in range(k):
+            assert np.allclose(o["px"][:, i], p[i], rtol=1e-13, atol=1e-300)
+            assert np.allclose(o["qx"][:, i], q[i], rtol=1e-13, atol=1e-300)
+
+
+def pin_bonus_searchsorted(lib):
+    """draft == target: every draft token is accepted for every u < 1, and the
+    bonus token is numpy.searchsorted(cumsum(p_k), r, 'right')."""
+    rng = np.random.default_rng(11)
+    for (V, k, tau) in [(5, 2, 1.0), (64, 3, 0.8), (1000, 4, 1.0)]:
+        B = 200
+        t = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+        d = np.ascontiguousarray(t[:, :k])
+        X = rng.integers(0, V, size=(B, k)).astype(np.int32)
+        u = np.float32(1.0 - 2.0 ** -24) * np.ones((B, k), np.float32)
+        u[::2] = rng.random((B // 2, k)).astype(np.float32)
+        r = rng.random(B).astype(np.float32)
+        o = svo.verify_stochastic(t, d, X, u, r, B=B, k=k, V=V, temperature=tau, lib=lib)
+        assert np.all(o["accept_len"] == k)
+        for b in range(B):
+            pk = softmax64(t[b, k], tau)
+            y = int(np.searchsorted(np.cumsum(pk), float(r[b]), side="right"))
+            assert o["tokens"][b, k] == y
+            assert np.array_equal(o["tokens"][b, :k], X[b])
+
+
+def pin_onehot_residual(lib):
+    """With a one-hot draft q = e_x: p/q = p(x); on rejection the residual is p
+    with token x removed and renormalised (a library searchsorted)."""
+    rng = np.random.default_rng(12)
+    V, k, B = 50, 1, 400
+    t = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+    X = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    d = np.full((B, k, V), -np.inf, np.float32)
+    d[np.arange(B), 0, X[:, 0]] = 0.0
+    u = rng.random((B, k)).astype(np.float32)
+    r = rng.random(B).astype(np.float32)
+    o = svo.verify_stochastic(t, d, X, u, r, B=B, k=k, V=V, lib=lib)
+    for b in range(B):
+        p0 = softmax64(t[b, 0])
+        x = X[b, 0]
+        accept = float(u[b, 0]) < p0[x]
+        assert o["accept_len"][b] == (1 if accept else 0)
+        if not accept:
+            w = p0.copy()
+            w[x] = 0.0
+            y = int(np.searchsorted(np.cumsum(w / w.sum()), float(r[b]), side="right"))
+            assert o["tokens"][b, 0] == y
+
+
+def pin_greedy_argmax(lib):
+    """Greedy = target argmax decoding; ties resolve to numpy.argmax's first
+    maximum; multi-candidate = brute force over candidates, lowest index on ties."""
+    rng = np.random.default_rng(13)
+    for (B, G, k, V) in [(50, 1, 3, 9), (40, 4, 2, 6), (30, 16, 4, 40)]:
+        t = rng.integers(-3, 3, size=(B, G, k + 1, V)).astype(np.float32)  # many ties
+        g = np.argmax(t, axis=-1)
+        X = rng.integers(0, V, size=(B, G, k)).astype(np.int32)
+        # make some candidates follow the argmax for a random number of steps
+        for b in range(B):
+            for c in range(G):
+                j = rng.integers(0, k + 1)
+                X[b, c, :j] = g[b, c, :j]
+        o = svo.verify_greedy(t, X, B=B, G=G, k=k, V=V, lib=lib)
+        for b in range(B):
+            acc = []
+            for c in range(G):
+                a = k
+                for i in range(k):
+                    if X[b, c, i] != g[b, c, i]:
+                        a = i
+                        break
+                acc.append(a)
+            cbest = int(np.argmax(acc))
+            a = acc[cbest]
+            assert o["accept_len"][b] == a
+            assert o["best_cand"][b] == cbest
+            assert np.array_equal(o["cand_accept"][b], acc)
+            assert np.array_equal(o["tokens"][b, :a + 1], g[b, cbest, :a + 1])
+            assert np.all(o["tokens"][b, a + 1:] == -1)
+
+
+def pin_greedy_bf16_ties(lib):
+    """bf16 rows with planted equal maxima: the first one wins."""
+    from draft_token_verification_10_amd.workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(14)
+    B, k, V = 64, 2, 300
+    t32 = (rng.standard_normal((B, k + 1, V)) * 3).astype(np.float32)
+    for b in range(B):
+        for i in range(k + 1):
+            pos = np.sort(rng.choice(V, size=3, replace=False))
+            t32[b, i, pos] = 20.0
+    tb = f32_to_bf16_bits(t32)
+    g = np.argmax(t32, axis=-1)
+    X = g[:, :k].astype(np.int32).copy()
+    o = svo.verify_greedy(tb, X, B=B, k=k, V=V, lib=lib)
+    assert np.all(o["accept_len"] == k)
+    assert np.array_equal(o["tokens"], g)
+
+
+# ---------------------------------------------------------- closed forms ----
+
+def pin_closed_forms(lib):
+    """Cases worked by hand with dyadic probabilities (exact in binary)."""
+    ninf = -np.inf
+    # V=2, k=1.  target row 0 = [0, 0] -> p0 = [1/2, 1/2]; draft = [0, -inf] ->
+    # q0 = [1, 0]; draft token 0: p/q = 1/2.  u = 1/4 accepts, u = 3/4 rejects.
+    # Residual max(0, p0 - q0) = [0, 1/2] -> always token 1.
+    # Target row 1 = [0, 0, ...]: bonus p1 = [1/2, 1/2]; r = 0.75 -> token 1.
+    t = np.array([[[0, 0], [0, 0]]] * 2, np.float32)
+    d = np.array([[[0, ninf]]] * 2, np.float32)
+    X = np.zeros((2, 1), np.int32)
+    u = np.array([[0.25], [0.75]], np.float32)
+    r = np.array([0.75, 0.0], np.float32)
+    o = svo.verify_stochastic(t, d, X, u, r, B=2, k=1, V=2, lib=lib)
+    assert o["accept_len"].tolist() == [1, 0]
+    assert o["tokens"].tolist() == [[0, 1], [1, -1]]
+    assert o["px"][:, 0].tolist() == [0.5, 0.5] and o["qx"][:, 0].tolist() == [1.0, 1.0]
+    # V=4 bonus from p = [1/4]*4: cumulative 1/4, 1/2, 3/4, 1.  The first
+    # cumulative strictly above r: r=0 -> 0, r=1/4 -> 1, r=0.6 -> 2, r=3/4 -> 3.
+    B = 4
+    t = np.zeros((B, 2, 4), np.float32)
+    d = np.zeros((B, 1, 4), np.float32)
+    X = np.zeros((B, 1), np.int32)
+    u = np.zeros((B, 1), np.float32)
+    r = np.array([0.0, 0.25, 0.6, 0.75], np.float32)
+    o = svo.verify_stochastic(t, d, X, u, r, B=B, k=1, V=4, lib=lib)
+    assert o["accept_len"].tolist() == [1] * 4
+    assert o["tokens"][:, 1].tolist() == [0, 1, 2, 3]
+    # temperature 1/2 doubles logits: target [ln 3 /2, 0] at tau=1/2 behaves
+    # like [ln 3, 0] -> p = [3/4, 1/4] (up to the rounding of ln 3 in float32);
+    # draft [0, 0] -> q = [1/2, 1/2]; token 1: p/q = 1/2.  u = 0.49 accepts,
+    # u = 0.51 rejects; residual max(0, p - q) = [1/4, 0] -> token 0.
+    l3 = np.float32(np.log(3.0) / 2)
+    t = np.array([[[l3, 0], [0, 0]]] * 2, np.float32)
+    d = np.zeros((2, 1, 2), np.float32)
+    X = np.ones((2, 1), np.int32)
+    u = np.array([[0.49], [0.51]], np.float32)
+    r = np.array([0.9, 0.9], np.float32)
+    o = svo.verify_stochastic(t, d, X, u, r, B=2, k=1, V=2, temperature=0.5, lib=lib)
+    assert o["accept_len"].tolist() == [1, 0]
+    assert o["tokens"][1].tolist() == [0, -1]
+    assert abs(o["px"][0, 0] - 0.25) < 1e-7 and o["qx"][0, 0] == 0.5
+    # a draft token outside the vocabulary has probability 0 and is rejected
+    t = np.zeros((1, 2, 4), np.float32)
+    d = np.zeros((1, 1, 4), np.float32)
+    o = svo.verify_stochastic(t, d, np.array([[7]], np.int32), np.zeros((1, 1), np.float32),
+                              np.array([0.1], np.float32), B=1, k=1, V=4, lib=lib)
+    assert o["accept_len"][0] == 0 and o["px"][0, 0] == 0 and o["qx"][0, 0] == 0
+    # p == q: residual is zero everywhere; the oracle then samples p itself
+    # (here uniform over 4): r = 0.6 -> token 2.
+    f = np.array([[svo.FORCE_REJECT]], np.int8)
+    o = svo.verify_stochastic(t, d, np.zeros((1, 1), np.int32), np.zeros((1, 1), np.float32),
+                              np.array([0.6], np.float32), B=1, k=1, V=4, force=f, lib=lib)
+    assert o["accept_len"][0] == 0 and o["tokens"][0].tolist() == [2, -1]
+
+
+# ------------------------------------------------------------------ P-INV ----
+
+def pin_invariants(lib):
+    rng = np.random.default_rng(15)
+    for (B, k, V, tau) in [(300, 4, 20, 1.0), (200, 8, 100, 0.7), (100, 1, 3, 1.0)]:
+        t = (rng.standard_normal((B, k + 1, V)) * 2).astype(np.float32)
+        d = (t[:, :k] + rng.standard_normal((B, k, V))).astype(np.float32)
+        X = rng.integers(0, V, size=(B, k)).astype(np.int32)
+        u = rng.random((B, k)).astype(np.float32)
+        r = rng.random(B).astype(np.float32)
+        o = svo.verify_stochastic(t, d, X, u, r, B=B, k=k, V=V, temperature=tau, lib=lib)
+        a = o["accept_len"]
+        assert np.all((a >= 0) & (a <= k))
+        for b in range(B):
+            ab = a[b]
+            assert np.array_equal(o["tokens"][b, :ab], X[b, :ab])
+            y = o["tokens"][b, ab]
+            assert 0 <= y < V
+            assert np.all(o["tokens"][b, ab + 1:] == -1)
+            if ab < k:
+                p = softmax64(t[b, ab], tau)
+                q = softmax64(d[b, ab], tau)
+                if np.any(p > q):
+                    assert p[y] > q[y], "corrective token outside the support of max(0, p-q)"
+            # accepted positions passed the test, the rejected one failed it
+            for i in range(ab):
+                assert float(u[b, i]) * o["qx"][b, i] < o["px"][b, i]
+            if ab < k:
+                assert not (float(u[b, ab]) * o["qx"][b, ab] < o["px"][b, ab])
+            # the emitted token's cell holds r and the cells sum to one
+            lo, hi = svo.emit_cdf(t, d, b=b, k=k, V=V, a=ab, y=y, temperature=tau, lib=lib)
+            assert lo <= float(r[b]) < hi + 1e-15
+            assert abs(lo - o["cdf_lo"][b]) < 1e-12 and abs(hi - o["cdf_hi"][b]) < 1e-12
+        lo, hi = svo.emit_cdf(t, d, b=0, k=k, V=V, a=0, y=V - 1, temperature=tau, lib=lib)
+        assert abs(hi - 1.0) < 1e-12
+
+
+ALL_PINS = [pin_enumeration, pin_softmax, pin_bonus_searchsorted, pin_onehot_residual,
+            pin_greedy_argmax, pin_greedy_bf16_ties, pin_closed_forms, pin_invariants]
