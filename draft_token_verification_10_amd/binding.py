@@ -1,0 +1,203 @@
+"""Thin ctypes binding of libspecverify on torch ROCm tensors.
+
+Argument marshalling only: shapes and strides are read from the tensors,
+pointers and the current HIP stream are passed to the C entry points of the
+same names, and the status code is turned into an exception.  Every step of
+the verification runs in the library's HIP kernels; there is no fallback.
+If ``libspecverify.so`` has not been built, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+SV_OK = 0
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+SV_MAX_K = 64
+SV_MAX_ROWS_PER_SEQ = 1024
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libspecverify.so (raises OSError when it is missing)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with __graft_entry__.build() "
+                      "(there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.sv_verify_stochastic.argtypes = [P, P, P, P, P, I, I, I, I64, I, ctypes.c_float,
+                                         P, P, P, P, SZ, P]
+    lib.sv_verify_stochastic.restype = I
+    lib.sv_verify_greedy.argtypes = [P, P, I, I, I, I, I64, I, P, P, P, P, SZ, P]
+    lib.sv_verify_greedy.restype = I
+    lib.sv_workspace_bytes.argtypes = [I, I, I, I]
+    lib.sv_workspace_bytes.restype = SZ
+    lib.sv_status_string.argtypes = [I]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libspecverify status {status}: {sv_status_string(status)}")
+
+
+def sv_status_string(status: int) -> str:
+    return load().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_bytes(B: int, G: int, k: int, V: int) -> int:
+    return int(load().sv_workspace_bytes(int(B), int(G), int(k), int(V)))
+
+
+# One zero-filled workspace per (device, stream); every call leaves it zeroed.
+_workspaces: dict = {}
+
+
+def workspace_for(nbytes: int, device: torch.device, stream: int) -> torch.Tensor:
+    key = (device.index, stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    """Element distance between consecutive logit rows; the rows of all
+    leading dimensions must be evenly spaced."""
+    if t.stride(-1) != 1:
+        raise ValueError("logit rows must be contiguous along the vocabulary")
+    for i in range(t.dim() - 2):
+        if t.size(i) > 1 and t.stride(i) != t.stride(i + 1) * t.size(i + 1):
+            raise ValueError("logit rows must be evenly spaced")
+    return int(t.stride(-2)) if t.dim() >= 2 else int(t.size(-1))
+
+
+def _dev(t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError("all tensors must live on the GPU")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_i32(t, shape, name):
+    _dev(t)
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape {tuple(shape)}")
+
+
+def _check_f32(t, shape, name):
+    _dev(t)
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+
+
+def sv_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                         draft_tokens: torch.Tensor, u_accept: torch.Tensor,
+                         u_sample: torch.Tensor, temperature: float = 1.0, *,
+                         accept_len: torch.Tensor | None = None,
+                         tokens: torch.Tensor | None = None,
+                         dbg_px_qx: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Stochastic verification.  target_logits [B][k+1][V], draft_logits
+    [B][k][V] (float32 or bfloat16; rows may be padded views), draft_tokens
+    int32 [B][k], u_accept float32 [B][k], u_sample float32 [B].  Returns
+    (accept_len int32 [B], tokens int32 [B][k+1]), written asynchronously on
+    the current stream (or ``stream``)."""
+    _dev(target_logits)
+    _dev(draft_logits)
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    if tuple(draft_logits.shape) != (B, k, V) or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("draft_logits must be [B][k][V] with the target's dtype")
+    rs = _row_stride(target_logits)
+    if B > 0 and _row_stride(draft_logits) != rs:
+        raise ValueError("target and draft rows must share one row stride")
+    _check_i32(draft_tokens, (B, k), "draft_tokens")
+    _check_f32(u_accept, (B, k), "u_accept")
+    _check_f32(u_sample, (B,), "u_sample")
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, k + 1), "tokens")
+    if dbg_px_qx is not None:
+        _check_f32(dbg_px_qx, (B, k, 2), "dbg_px_qx")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, 1, k, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_verify_stochastic(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+        _ptr(u_sample), B, k, V, rs, _dtype_code(target_logits), float(temperature),
+        _ptr(accept_len), _ptr(tokens), _ptr(dbg_px_qx), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens
+
+
+def sv_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
+                     accept_len: torch.Tensor | None = None,
+                     tokens: torch.Tensor | None = None,
+                     best_cand: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """Greedy verification.  target_logits [B][k+1][V] with draft_tokens
+    [B][k], or [B][G][k+1][V] with [B][G][k] for G candidates.  Returns
+    (accept_len [B], tokens [B][k+1], best_cand [B])."""
+    _dev(target_logits)
+    if target_logits.dim() == 3:
+        B, k1, V = target_logits.shape
+        G = 1
+    else:
+        B, G, k1, V = target_logits.shape
+    k = k1 - 1
+    rs = _row_stride(target_logits)
+    _check_i32(draft_tokens, (B, k) if target_logits.dim() == 3 else (B, G, k), "draft_tokens")
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    if best_cand is None:
+        best_cand = torch.empty(B, dtype=torch.int32, device=dev)
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, k + 1), "tokens")
+    _check_i32(best_cand, (B,), "best_cand")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, G, k, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_verify_greedy(
+        _ptr(target_logits), _ptr(draft_tokens), B, G, k, V, rs, _dtype_code(target_logits),
+        _ptr(accept_len), _ptr(tokens), _ptr(best_cand), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens, best_cand

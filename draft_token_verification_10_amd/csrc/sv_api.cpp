@@ -1,0 +1,182 @@
+// sv_api.cpp -- host side of libspecverify: argument checks, the launch
+// plan, and the exported C entry points declared in include/specverify.h.
+// Every check runs before anything is launched, so an error leaves all
+// buffers untouched.
+#include "specverify.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace {
+
+// Largest grid: x-dimension threads must fit in 32 bits at 256 per group.
+constexpr long long kMaxGrid = 16777215LL;
+// Largest vocabulary: keeps every in-row element index and slice bound in int.
+constexpr int kMaxV = 1 << 28;
+
+int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_shape(int B, int G, int k, int V, int64_t row_stride) {
+    if (B < 0 || G < 1 || k < 1 || V < 1) return SV_ERR_SHAPE;
+    if (k > SV_MAX_K || V > kMaxV) return SV_ERR_SHAPE;
+    if ((long long)G * (k + 1) > SV_MAX_ROWS_PER_SEQ) return SV_ERR_SHAPE;
+    if (row_stride < V) return SV_ERR_SHAPE;
+    return SV_OK;
+}
+
+struct Plan {
+    int rows_per_seq;
+    int S;
+    int slice_len;
+    bool vec;
+    size_t ws_bytes;
+};
+
+int make_plan(int B, int rows_per_seq, int V, int64_t row_stride, int dtype,
+              const void* const* row_bases, int n_bases, Plan* pl) {
+    const int es = elem_size(dtype);
+    bool vec = ((row_stride * es) % 16) == 0;
+    for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
+    const int E = vec ? 16 / es : 1;
+    const int S0 = sv::plan_slices((long long)B * rows_per_seq, V);
+    // slice length: a whole number of chunks, then drop empty slices
+    int chunks = (V + E - 1) / E;
+    int per = (chunks + S0 - 1) / S0;
+    int slice_len = per * E;
+    int S = (V + slice_len - 1) / slice_len;
+    if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
+    pl->rows_per_seq = rows_per_seq;
+    pl->S = S;
+    pl->slice_len = slice_len;
+    pl->vec = vec;
+    pl->ws_bytes = sv::workspace_bytes_for(B, rows_per_seq, S);
+    return SV_OK;
+}
+
+int check_workspace(const void* ws, size_t bytes, const Plan& pl) {
+    if (((uintptr_t)ws & 255u) != 0) return SV_ERR_WORKSPACE;
+    if (bytes < pl.ws_bytes) return SV_ERR_WORKSPACE;
+    return SV_OK;
+}
+
+}  // namespace
+
+// The library is built with hidden visibility; only the C ABI is exported.
+#pragma GCC visibility push(default)
+extern "C" {
+
+size_t sv_workspace_bytes(int B, int G, int k, int V) {
+    if (check_shape(B, G, k, V, V) != SV_OK) return 0;
+    // Upper bound over both entry points and both load paths: the slice count
+    // before rounding to whole chunks is never exceeded.
+    const int rows_s = 2 * k + 1;
+    const int rows_g = G * (k + 1);
+    const size_t s = sv::workspace_bytes_for(B, rows_s, sv::plan_slices((long long)B * rows_s, V));
+    const size_t g = sv::workspace_bytes_for(B, rows_g, sv::plan_slices((long long)B * rows_g, V));
+    return s > g ? s : g;
+}
+
+const char* sv_status_string(int status) {
+    switch (status) {
+        case SV_OK: return "success";
+        case SV_ERR_NULL: return "a required pointer is NULL";
+        case SV_ERR_SHAPE: return "invalid shape (B, G, k, V or row_stride out of range)";
+        case SV_ERR_DTYPE: return "unsupported logit dtype";
+        case SV_ERR_TEMPERATURE: return "temperature must be positive and finite";
+        case SV_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+        case SV_ERR_HIP: return "the HIP runtime refused the kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* u_accept,
+                         const float* u_sample, int B, int k, int V, int64_t row_stride,
+                         int dtype, float temperature, int32_t* accept_len, int32_t* tokens,
+                         float* dbg_px_qx, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    int st = check_shape(B, 1, k, V, row_stride);
+    if (st != SV_OK) return st;
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    const double c = 1.4426950408889634 / (double)temperature;
+    if (!(temperature > 0.0f) || !isfinite(temperature) || !isfinite((float)c))
+        return SV_ERR_TEMPERATURE;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
+        !accept_len || !tokens || !workspace)
+        return SV_ERR_NULL;
+    const void* bases[2] = {target_logits, draft_logits};
+    Plan pl;
+    st = make_plan(B, 2 * k + 1, V, row_stride, dtype, bases, 2, &pl);
+    if (st != SV_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, pl);
+    if (st != SV_OK) return st;
+
+    sv::Params p = {};
+    p.target = target_logits;
+    p.draft = draft_logits;
+    p.tokens_in = draft_tokens;
+    p.u_accept = u_accept;
+    p.u_sample = u_sample;
+    p.accept_len = accept_len;
+    p.tokens_out = tokens;
+    p.best_cand = nullptr;
+    p.dbg = dbg_px_qx;
+    p.counters = static_cast<int*>(workspace);
+    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sv::counter_bytes(B));
+    p.row_stride = row_stride;
+    p.B = B;
+    p.G = 1;
+    p.k = k;
+    p.V = V;
+    p.rows_per_seq = pl.rows_per_seq;
+    p.S = pl.S;
+    p.slice_len = pl.slice_len;
+    p.c = (float)c;
+    return sv::launch_stochastic(p, dtype, pl.vec, stream) == 0 ? SV_OK : SV_ERR_HIP;
+}
+
+int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int G,
+                     int k, int V, int64_t row_stride, int dtype, int32_t* accept_len,
+                     int32_t* tokens, int32_t* best_cand, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    int st = check_shape(B, G, k, V, row_stride);
+    if (st != SV_OK) return st;
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (B == 0) return SV_OK;
+    if (!target_logits || !draft_tokens || !accept_len || !tokens || !workspace)
+        return SV_ERR_NULL;
+    const void* bases[1] = {target_logits};
+    Plan pl;
+    st = make_plan(B, G * (k + 1), V, row_stride, dtype, bases, 1, &pl);
+    if (st != SV_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, pl);
+    if (st != SV_OK) return st;
+
+    sv::Params p = {};
+    p.target = target_logits;
+    p.draft = nullptr;
+    p.tokens_in = draft_tokens;
+    p.accept_len = accept_len;
+    p.tokens_out = tokens;
+    p.best_cand = best_cand;
+    p.counters = static_cast<int*>(workspace);
+    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sv::counter_bytes(B));
+    p.row_stride = row_stride;
+    p.B = B;
+    p.G = G;
+    p.k = k;
+    p.V = V;
+    p.rows_per_seq = pl.rows_per_seq;
+    p.S = pl.S;
+    p.slice_len = pl.slice_len;
+    p.c = 0.0f;
+    return sv::launch_greedy(p, dtype, pl.vec, stream) == 0 ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

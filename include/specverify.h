@@ -1,0 +1,154 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the speculative-decoding
+ * verification step on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  A draft model proposes k tokens per sequence; the target
+ * model produces logits for the k draft positions plus one more.  The
+ * verification step decides how many draft tokens the target accepts and
+ * emits one further token, so k drafts yield between 1 and k+1 tokens
+ * (Perplexity, "Accelerating Sonar through speculation", section
+ * "Špekulatívne dekódovanie": the acceptance stage keeps the longest
+ * acceptable draft prefix and the target-generation stage samples the closing
+ * token from the target's logits at the first mismatch or after the last
+ * draft token).  Acceptance compares the full target and draft distributions
+ * (same page, section "Cieľ-Návrh"), and one verifier serves every drafting
+ * scheme -- draft model, MTP head, n-gram candidates -- since all of them only
+ * change how the logits are produced (same page, section "MTP").
+ *
+ * Two entry points, one per decision rule:
+ *
+ *   sv_verify_stochastic -- lossless speculative sampling.  With
+ *     p_i = softmax(target_i / T) and q_i = softmax(draft_i / T) over the whole
+ *     vocabulary, draft token x_i is accepted when u_i * q_i(x_i) < p_i(x_i)
+ *     (u_i < min(1, p_i/q_i)); a is the first rejected position (k if none).
+ *     At a < k the extra token is drawn from max(0, p_a - q_a) renormalised
+ *     (from p_a if that is zero everywhere); at a == k it is drawn from p_k.
+ *     Drawing is by inverse CDF over ascending token index with the caller's
+ *     uniform r: the first token whose cumulative mass exceeds r.  This rule
+ *     is the one that keeps the target model's output distribution unchanged,
+ *     which is the aim the pages set (aidevelopers.cz, "Zkoumání
+ *     spekulativního dekódování v vLLM na AMD GPU", section "Základní
+ *     autoregresivní dekódování").
+ *
+ *   sv_verify_greedy -- accept while the draft token equals the target
+ *     argmax (lowest index among equal maxima); the extra token is the target
+ *     argmax at the first mismatch or at position k.  With G > 1 candidate
+ *     token sequences per sequence (n-gram verification of Lookahead decoding,
+ *     gateex.cc, section "A descodificação avançada quebra a dependência da
+ *     ordem", items 2 and 4: many guessed n-grams are checked in one step and
+ *     the longest verified one is kept) the candidate with the longest
+ *     accepted prefix wins, lowest candidate index on ties.
+ *
+ * Memory and ownership.  Every pointer is a device pointer owned by the
+ * caller (u_accept, u_sample, tokens, outputs and workspace included).  The
+ * library allocates nothing and keeps no state between calls.  Logits are
+ * float32 or bfloat16, row-major, one row of V entries every row_stride
+ * elements (row_stride >= V; padding entries are never read).  Rows:
+ *   stochastic: target row i of sequence b at (b*(k+1) + i) * row_stride,
+ *               draft  row i of sequence b at (b*k     + i) * row_stride;
+ *   greedy:     target row i of candidate c of sequence b at
+ *               ((b*G + c)*(k+1) + i) * row_stride.
+ * Rows whose start is 16-byte aligned (base pointer 16-byte aligned and
+ * row_stride * element size a multiple of 16) take the vector path; others
+ * are read element by element (correct, slower).
+ *
+ * Ordering.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ * null stream) and never synchronise with the host: accept_len and tokens are
+ * valid once the stream reaches the end of the call.  Reading them on the
+ * host is the one GPU-to-CPU crossing of a decoding step (Perplexity, same
+ * page, section "Inferencia so špekulatívnym dekódovaním": the accepted
+ * length decides the next step's shape).
+ *
+ * Workspace.  sv_workspace_bytes() gives the size for a shape; pass at least
+ * that many bytes, 256-byte aligned, ZERO-FILLED before its first use.  Every
+ * call returns it to all zeros by the time it completes, so one workspace
+ * serves any sequence of calls on one stream.  Two calls that overlap in time
+ * on the same workspace race.
+ *
+ * Errors.  Arguments are checked on the host before anything is launched; on
+ * an error nothing is written and a negative SV_ERR_* status is returned.
+ * Values inside device buffers are not checked: u in [0,1), r in [0,1),
+ * logits finite or -inf with at least one finite entry per row (NaN and +inf
+ * are undefined).  A draft token outside [0, V) is defined behaviour: it has
+ * probability 0 under both distributions and is rejected (greedy: it never
+ * matches).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SV_OK 0
+#define SV_ERR_NULL (-1)        /* a required pointer is NULL               */
+#define SV_ERR_SHAPE (-2)       /* B < 0, G/k/V < 1, k > SV_MAX_K, G*(k+1) > */
+                                /* SV_MAX_ROWS_PER_SEQ, row_stride < V, or   */
+                                /* the launch grid would be too large        */
+#define SV_ERR_DTYPE (-3)       /* dtype is not SV_DTYPE_F32/SV_DTYPE_BF16  */
+#define SV_ERR_TEMPERATURE (-4) /* temperature <= 0 or not finite           */
+#define SV_ERR_WORKSPACE (-5)   /* workspace smaller than required or not   */
+                                /* 256-byte aligned                         */
+#define SV_ERR_HIP (-6)         /* the HIP runtime refused the launch       */
+
+/* Logit element types. */
+#define SV_DTYPE_F32 0
+#define SV_DTYPE_BF16 1
+
+/* Limits. */
+#define SV_MAX_K 64               /* draft tokens per sequence (candidate)   */
+#define SV_MAX_ROWS_PER_SEQ 1024  /* G*(k+1) in greedy mode                 */
+
+/*
+ * Stochastic verification of B sequences.
+ *   target_logits  [B][k+1] rows of V logits (see layout above)
+ *   draft_logits   [B][k]   rows, same dtype and row_stride as the target
+ *   draft_tokens   int32 [B][k]
+ *   u_accept       float [B][k]  acceptance uniforms, one per position
+ *   u_sample       float [B]     one uniform per sequence for the extra token
+ *   temperature    divides target and draft logits alike
+ *   accept_len     out int32 [B]: accepted draft tokens a in [0, k]
+ *   tokens         out int32 [B][k+1]: x_0..x_{a-1}, the extra token, then -1
+ *   dbg_px_qx      optional out float [B][k][2]: p_i(x_i), q_i(x_i) for every
+ *                  position (NULL to skip)
+ * B == 0 is a no-op that returns SV_OK.
+ */
+int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* u_accept,
+                         const float* u_sample, int B, int k, int V,
+                         int64_t row_stride, int dtype, float temperature,
+                         int32_t* accept_len, int32_t* tokens,
+                         float* dbg_px_qx, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy verification of B sequences with G >= 1 candidates each.
+ *   target_logits  [B][G][k+1] rows of V logits
+ *   draft_tokens   int32 [B][G][k]
+ *   accept_len     out int32 [B]: accepted tokens of the winning candidate
+ *   tokens         out int32 [B][k+1]: its tokens, the target argmax after
+ *                  them, then -1
+ *   best_cand      optional out int32 [B]: index of the winning candidate
+ * B == 0 is a no-op that returns SV_OK.
+ */
+int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
+                     int B, int G, int k, int V, int64_t row_stride, int dtype,
+                     int32_t* accept_len, int32_t* tokens, int32_t* best_cand,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that suffice for either entry point at this shape
+ * (G = 1 for stochastic calls).  Returns 0 for an invalid shape. */
+size_t sv_workspace_bytes(int B, int G, int k, int V);
+
+/* Static, human-readable text for a status code. */
+const char* sv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,155 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_token_verification_10_amd import binding
+from draft_token_verification_10_amd.build import INCLUDE, LIB_PATH
+
+HEADER = os.path.join(INCLUDE, "specverify.h")
+
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_TEMPERATURE, SV_ERR_WORKSPACE, SV_ERR_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in
+            re.finditer(r"#define\s+(SV_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        pytest.skip("libspecverify.so not built")
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == ["sv_status_string", "sv_verify_greedy", "sv_verify_stochastic",
+                     "sv_workspace_bytes"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    c = header_constants()
+    assert c["SV_OK"] == SV_OK and c["SV_ERR_NULL"] == SV_ERR_NULL
+    assert c["SV_ERR_SHAPE"] == SV_ERR_SHAPE and c["SV_ERR_DTYPE"] == SV_ERR_DTYPE
+    assert c["SV_ERR_TEMPERATURE"] == SV_ERR_TEMPERATURE
+    assert c["SV_ERR_WORKSPACE"] == SV_ERR_WORKSPACE and c["SV_ERR_HIP"] == SV_ERR_HIP
+    assert c["SV_DTYPE_F32"] == binding.SV_DTYPE_F32
+    assert c["SV_DTYPE_BF16"] == binding.SV_DTYPE_BF16
+    assert c["SV_MAX_K"] == binding.SV_MAX_K
+    assert c["SV_MAX_ROWS_PER_SEQ"] == binding.SV_MAX_ROWS_PER_SEQ
+
+
+def test_status_strings(lib):
+    seen = set()
+    for st in (SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_TEMPERATURE,
+               SV_ERR_WORKSPACE, SV_ERR_HIP):
+        s = lib.sv_status_string(st).decode()
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 7
+    assert lib.sv_status_string(12345).decode() == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.sv_workspace_bytes
+    assert f(0, 1, 1, 1) == 0 or f(0, 1, 1, 1) % 256 == 0
+    for args in [(256, 1, 8, 128256), (64, 1, 4, 128256), (1, 1, 4, 32000), (32, 16, 4, 32000),
+                 (512, 1, 3, 129280)]:
+        n = f(*args)
+        assert n > 0 and n % 8 == 0
+    # bad shapes
+    for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, 0, 10), (1, 1, 1, 0), (1, 1, 65, 10),
+                 (1, 600, 1, 10)]:
+        assert f(*args) == 0
+    # larger batches never need less
+    assert f(512, 1, 8, 128256) >= f(256, 1, 8, 128256)
+
+
+# Fake, well-aligned device addresses: the checks below fail before any
+# pointer is used, so nothing is dereferenced or launched.
+A = ctypes.c_void_p(1 << 20)
+WS = ctypes.c_void_p(1 << 21)
+
+
+def stoch(lib, **kw):
+    args = dict(t=A, d=A, x=A, ua=A, us=A, B=2, k=3, V=100, rs=100, dtype=1, tau=1.0,
+                al=A, tok=A, dbg=None, ws=WS, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_stochastic(args["t"], args["d"], args["x"], args["ua"], args["us"],
+                                    args["B"], args["k"], args["V"], args["rs"], args["dtype"],
+                                    args["tau"], args["al"], args["tok"], args["dbg"], args["ws"],
+                                    args["wsb"], args["stream"])
+
+
+def greedy(lib, **kw):
+    args = dict(t=A, x=A, B=2, G=1, k=3, V=100, rs=100, dtype=0, al=A, tok=A, bc=None, ws=WS,
+                wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_greedy(args["t"], args["x"], args["B"], args["G"], args["k"],
+                                args["V"], args["rs"], args["dtype"], args["al"], args["tok"],
+                                args["bc"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("field", ["t", "d", "x", "ua", "us", "al", "tok", "ws"])
+def test_stochastic_null(lib, field):
+    assert stoch(lib, **{field: None}) == SV_ERR_NULL
+
+
+@pytest.mark.parametrize("field", ["t", "x", "al", "tok", "ws"])
+def test_greedy_null(lib, field):
+    assert greedy(lib, **{field: None}) == SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(k=0), dict(k=65), dict(V=0), dict(rs=99),
+                                dict(V=(1 << 28) + 1, rs=(1 << 28) + 1)])
+def test_stochastic_shape(lib, kw):
+    assert stoch(lib, **kw) == SV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("kw", [dict(B=-3), dict(G=0), dict(k=0), dict(V=-5), dict(rs=10),
+                                dict(G=300, k=3), dict(G=16, k=64)])
+def test_greedy_shape(lib, kw):
+    assert greedy(lib, **kw) == SV_ERR_SHAPE
+
+
+def test_grid_too_large(lib):
+    # 2^24 workgroups would overflow the 32-bit launch size
+    assert greedy(lib, B=1 << 21, G=1, k=7, V=10, rs=10) == SV_ERR_SHAPE
+
+
+def test_dtype(lib):
+    assert stoch(lib, dtype=2) == SV_ERR_DTYPE
+    assert greedy(lib, dtype=-1) == SV_ERR_DTYPE
+
+
+@pytest.mark.parametrize("tau", [0.0, -1.0, float("inf"), float("nan"), 1e-45])
+def test_temperature(lib, tau):
+    assert stoch(lib, tau=tau) == SV_ERR_TEMPERATURE
+
+
+def test_workspace_checks(lib):
+    need = lib.sv_workspace_bytes(2, 1, 3, 100)
+    assert stoch(lib, wsb=need - 1) == SV_ERR_WORKSPACE
+    assert stoch(lib, ws=ctypes.c_void_p((1 << 21) + 16)) == SV_ERR_WORKSPACE
+    assert greedy(lib, wsb=8) == SV_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert stoch(lib, B=0, t=None, d=None, x=None, ua=None, us=None, al=None, tok=None,
+                 ws=None, wsb=0) == SV_OK
+    assert greedy(lib, B=0, t=None, x=None, al=None, tok=None, ws=None, wsb=0) == SV_OK
