@@ -63,17 +63,24 @@ def sv_workspace_bytes(B: int, G: int, k: int, V: int) -> int:
     return int(load().sv_workspace_bytes(int(B), int(G), int(k), int(V)))
 
 
-# One zero-filled workspace per (device, stream); every call leaves it zeroed.
+# One cached workspace per (device, stream), grown on demand.  Its contents
+# never matter between calls.
 _workspaces: dict = {}
 
 
-def workspace_for(nbytes: int, device: torch.device, stream: int) -> torch.Tensor:
+def workspace_for(nbytes: int, device: torch.device, stream: int):
+    if nbytes == 0:
+        return None
     key = (device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def _ws_bytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -156,8 +163,8 @@ def sv_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor
     st = load().sv_verify_stochastic(
         _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
         _ptr(u_sample), B, k, V, rs, _dtype_code(target_logits), float(temperature),
-        _ptr(accept_len), _ptr(tokens), _ptr(dbg_px_qx), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), ctypes.c_void_p(s))
+        _ptr(accept_len), _ptr(tokens), _ptr(dbg_px_qx), _ptr(workspace), _ws_bytes(workspace),
+        ctypes.c_void_p(s))
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accept_len, tokens
@@ -196,8 +203,8 @@ def sv_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
         workspace = workspace_for(need, dev, s)
     st = load().sv_verify_greedy(
         _ptr(target_logits), _ptr(draft_tokens), B, G, k, V, rs, _dtype_code(target_logits),
-        _ptr(accept_len), _ptr(tokens), _ptr(best_cand), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), ctypes.c_void_p(s))
+        _ptr(accept_len), _ptr(tokens), _ptr(best_cand), _ptr(workspace), _ws_bytes(workspace),
+        ctypes.c_void_p(s))
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accept_len, tokens, best_cand

@@ -11,8 +11,10 @@
 
 namespace {
 
-// Largest grid: x-dimension threads must fit in 32 bits at 256 per group.
+// Largest grids: the x-dimension thread count must fit in 32 bits (256
+// threads per row-split statistics group, 1024 per sequence-resident group).
 constexpr long long kMaxGrid = 16777215LL;
+constexpr long long kMaxSeqGrid = 4194303LL;
 // Largest vocabulary: keeps every in-row element index and slice bound in int.
 constexpr int kMaxV = 1 << 28;
 
@@ -29,6 +31,7 @@ int check_shape(int B, int G, int k, int V, int64_t row_stride) {
 }
 
 struct Plan {
+    bool seq;  // sequence-resident layout (no workspace)
     int rows_per_seq;
     int S;
     int slice_len;
@@ -36,31 +39,47 @@ struct Plan {
     size_t ws_bytes;
 };
 
-int make_plan(int B, int rows_per_seq, int V, int64_t row_stride, int dtype,
+int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dtype,
               const void* const* row_bases, int n_bases, Plan* pl) {
     const int es = elem_size(dtype);
     bool vec = ((row_stride * es) % 16) == 0;
     for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
+    pl->seq = sv::use_seq_resident(B, G);
+    pl->rows_per_seq = rows_per_seq;
+    pl->vec = vec;
+    if (pl->seq) {
+        pl->S = 1;
+        pl->slice_len = V;
+        pl->ws_bytes = 0;
+        return B > kMaxSeqGrid ? SV_ERR_SHAPE : SV_OK;
+    }
     const int E = vec ? 16 / es : 1;
     const int S0 = sv::plan_slices((long long)B * rows_per_seq, V);
     // slice length: a whole number of chunks, then drop empty slices
-    int chunks = (V + E - 1) / E;
-    int per = (chunks + S0 - 1) / S0;
-    int slice_len = per * E;
-    int S = (V + slice_len - 1) / slice_len;
+    const int chunks = (V + E - 1) / E;
+    const int per = (chunks + S0 - 1) / S0;
+    const int slice_len = per * E;
+    const int S = (V + slice_len - 1) / slice_len;
     if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
-    pl->rows_per_seq = rows_per_seq;
     pl->S = S;
     pl->slice_len = slice_len;
-    pl->vec = vec;
     pl->ws_bytes = sv::workspace_bytes_for(B, rows_per_seq, S);
     return SV_OK;
 }
 
 int check_workspace(const void* ws, size_t bytes, const Plan& pl) {
+    if (pl.ws_bytes == 0) return SV_OK;
+    if (!ws) return SV_ERR_NULL;
     if (((uintptr_t)ws & 255u) != 0) return SV_ERR_WORKSPACE;
     if (bytes < pl.ws_bytes) return SV_ERR_WORKSPACE;
     return SV_OK;
+}
+
+// Workspace bytes for one entry point at this shape (an upper bound over the
+// load paths: the slice count before rounding to whole chunks).
+size_t workspace_need(int B, int G, int rows_per_seq, int V) {
+    if (sv::use_seq_resident(B, G)) return 0;
+    return sv::workspace_bytes_for(B, rows_per_seq, sv::plan_slices((long long)B * rows_per_seq, V));
 }
 
 }  // namespace
@@ -71,12 +90,9 @@ extern "C" {
 
 size_t sv_workspace_bytes(int B, int G, int k, int V) {
     if (check_shape(B, G, k, V, V) != SV_OK) return 0;
-    // Upper bound over both entry points and both load paths: the slice count
-    // before rounding to whole chunks is never exceeded.
-    const int rows_s = 2 * k + 1;
-    const int rows_g = G * (k + 1);
-    const size_t s = sv::workspace_bytes_for(B, rows_s, sv::plan_slices((long long)B * rows_s, V));
-    const size_t g = sv::workspace_bytes_for(B, rows_g, sv::plan_slices((long long)B * rows_g, V));
+    // Enough for either entry point: stochastic (one candidate) and greedy.
+    const size_t s = workspace_need(B, 1, 2 * k + 1, V);
+    const size_t g = workspace_need(B, G, G * (k + 1), V);
     return s > g ? s : g;
 }
 
@@ -87,7 +103,7 @@ const char* sv_status_string(int status) {
         case SV_ERR_SHAPE: return "invalid shape (B, G, k, V or row_stride out of range)";
         case SV_ERR_DTYPE: return "unsupported logit dtype";
         case SV_ERR_TEMPERATURE: return "temperature must be positive and finite";
-        case SV_ERR_WORKSPACE: return "workspace too small or not 256-byte aligned";
+        case SV_ERR_WORKSPACE: return "workspace smaller than sv_workspace_bytes() or not 256-byte aligned";
         case SV_ERR_HIP: return "the HIP runtime refused the kernel launch";
         default: return "unknown status";
     }
@@ -107,11 +123,11 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
         return SV_ERR_TEMPERATURE;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
-        !accept_len || !tokens || !workspace)
+        !accept_len || !tokens)
         return SV_ERR_NULL;
     const void* bases[2] = {target_logits, draft_logits};
     Plan pl;
-    st = make_plan(B, 2 * k + 1, V, row_stride, dtype, bases, 2, &pl);
+    st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, bases, 2, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;
@@ -126,8 +142,7 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
     p.tokens_out = tokens;
     p.best_cand = nullptr;
     p.dbg = dbg_px_qx;
-    p.counters = static_cast<int*>(workspace);
-    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sv::counter_bytes(B));
+    p.part = static_cast<float*>(workspace);
     p.row_stride = row_stride;
     p.B = B;
     p.G = 1;
@@ -137,7 +152,7 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
     p.S = pl.S;
     p.slice_len = pl.slice_len;
     p.c = (float)c;
-    return sv::launch_stochastic(p, dtype, pl.vec, stream) == 0 ? SV_OK : SV_ERR_HIP;
+    return sv::launch_stochastic(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
 }
 
 int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int G,
@@ -148,11 +163,10 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     if (st != SV_OK) return st;
     if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
     if (B == 0) return SV_OK;
-    if (!target_logits || !draft_tokens || !accept_len || !tokens || !workspace)
-        return SV_ERR_NULL;
+    if (!target_logits || !draft_tokens || !accept_len || !tokens) return SV_ERR_NULL;
     const void* bases[1] = {target_logits};
     Plan pl;
-    st = make_plan(B, G * (k + 1), V, row_stride, dtype, bases, 1, &pl);
+    st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, bases, 1, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;
@@ -164,8 +178,7 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     p.accept_len = accept_len;
     p.tokens_out = tokens;
     p.best_cand = best_cand;
-    p.counters = static_cast<int*>(workspace);
-    p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sv::counter_bytes(B));
+    p.part = static_cast<float*>(workspace);
     p.row_stride = row_stride;
     p.B = B;
     p.G = G;
@@ -175,7 +188,7 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     p.S = pl.S;
     p.slice_len = pl.slice_len;
     p.c = 0.0f;
-    return sv::launch_greedy(p, dtype, pl.vec, stream) == 0 ? SV_OK : SV_ERR_HIP;
+    return sv::launch_greedy(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
 }
 
 }  // extern "C"

@@ -8,16 +8,31 @@
 
 namespace sv {
 
-// Each logit row is cut into S slices and every (row, slice) pair is one
-// workgroup of the streaming pass.  S is raised above 1 only when the batch
-// has too few rows to give every compute unit several workgroups.
-constexpr long long kTargetItems = 2048;  // about 8 workgroups per CU (256 CUs)
-constexpr int kMinSliceElems = 4096;      // never cut a row finer than this
-constexpr int kMaxSlices = 64;
 constexpr int kMaxK = 64;
 constexpr int kMaxRowsPerSeq = 1024;
 
-// Slices per row for `rows` rows of V logits.
+// Two ways to lay the work out on the GPU:
+//
+//  * sequence-resident: one 1024-thread workgroup owns one sequence, streams
+//    all of its rows and finishes it in place.  Nothing crosses workgroups,
+//    so there are no atomics, fences or workspace.  Used when the batch alone
+//    fills the machine (single candidate, B >= kSeqResidentMinB).
+//
+//  * row-split: a statistics kernel gives every (row, slice) its own
+//    workgroup and writes 8 bytes per item to the workspace; a finishing
+//    kernel (one workgroup per sequence) merges them, decides and samples.
+//    The kernel boundary makes the statistics visible.  Used for small
+//    batches and for several candidates per sequence.
+constexpr int kSeqResidentMinB = 192;
+
+inline bool use_seq_resident(int B, int G) { return G == 1 && B >= kSeqResidentMinB; }
+
+// Row-split plan: each row is cut into S slices, S raised above 1 only when
+// there are too few rows to give every compute unit several workgroups.
+constexpr long long kTargetItems = 2048;  // about 8 workgroups per CU (256 CUs)
+constexpr int kMinSliceElems = 4096;      // never cut a row finer than this
+constexpr int kMaxSlices = 64;
+
 inline int plan_slices(long long rows, int V) {
     long long s = 1;
     if (rows > 0 && rows < kTargetItems) s = (kTargetItems + rows - 1) / rows;
@@ -28,13 +43,9 @@ inline int plan_slices(long long rows, int V) {
     return (int)s;
 }
 
-// Bytes reserved for the per-sequence arrival counters (int32 [B]).
-inline size_t counter_bytes(int B) { return ((size_t)B * 4 + 255) / 256 * 256; }
-
-// Bytes of the workspace: counters, then float2 partial statistics
-// [B][rows_per_seq][S].
+// Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S].
 inline size_t workspace_bytes_for(int B, int rows_per_seq, int S) {
-    return counter_bytes(B) + (size_t)B * rows_per_seq * S * 8;
+    return (size_t)B * rows_per_seq * S * 8;
 }
 
 struct Params {
@@ -47,19 +58,19 @@ struct Params {
     int32_t* tokens_out;
     int32_t* best_cand;
     float* dbg;
-    int* counters;        // [B], zero between calls
-    float* part;          // [B][rows_per_seq][S][2]
+    float* part;          // row-split only: [B][rows_per_seq][S][2]
     long long row_stride; // elements
     int B, G, k, V;
     int rows_per_seq;     // stochastic 2k+1, greedy G(k+1)
-    int S;                // slices per row
-    int slice_len;        // elements per slice
+    int S;                // row-split: slices per row
+    int slice_len;        // row-split: elements per slice
     float c;              // log2(e) / temperature
 };
 
-// Launchers (sv_kernels.hip).  dtype: 0 float32, 1 bfloat16; vec: rows start
-// on 16-byte boundaries.  Return a hipError_t value (0 = success).
-int launch_stochastic(const Params& p, int dtype, bool vec, void* stream);
-int launch_greedy(const Params& p, int dtype, bool vec, void* stream);
+// Launchers (sv_kernels.hip).  dtype: 0 float32, 1 bfloat16; vec: every row
+// starts on a 16-byte boundary; seq_resident: which layout (see above).
+// Return a hipError_t value (0 = success).
+int launch_stochastic(const Params& p, int dtype, bool vec, bool seq_resident, void* stream);
+int launch_greedy(const Params& p, int dtype, bool vec, bool seq_resident, void* stream);
 
 }  // namespace sv

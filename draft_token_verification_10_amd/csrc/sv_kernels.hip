@@ -1,17 +1,21 @@
 // sv_kernels.hip -- the verification step on gfx950 (MI355X).
 //
-// One kernel per decision rule.  Every workgroup first streams one slice of
-// one logit row from HBM once, with 16-byte loads, and reduces it to 8 bytes
-// of statistics:
+// Every logit row is streamed from HBM once with 16-byte loads and reduced
+// to a few bytes of statistics:
 //   stochastic: a reference R and Z = sum_v 2^(x_v*c - R), c = log2(e)/T,
-//               kept with a lazily raised R so the exponentials never
-//               overflow (an online softmax normaliser);
-//   greedy:     the slice maximum and the lowest index holding it.
-// The workgroup then bumps its sequence's arrival counter; the one that
-// arrives last merges the sequence's statistics and finishes the sequence on
-// the spot: acceptance test, accept-prefix scan, the extra token, outputs.
-// Nothing is a dense contraction, so no MFMA is used; the pass is bound by
-// HBM bandwidth (and, for bfloat16 stochastic rows, by VALU/exp issue).
+//               with R raised lazily so no exponential overflows (an online
+//               softmax normaliser: p(v) = 2^(x_v*c - R) / Z);
+//   greedy:     the row maximum and the lowest index holding it.
+// From those, one workgroup per sequence computes p_i(x_i) and q_i(x_i),
+// runs the acceptance test and the accept-prefix scan, and draws the
+// corrective or bonus token by inverse CDF with block-wide LDS scans (the
+// only step that reads logits a second time: one or two rows per sequence).
+// Nothing is a dense contraction, so no MFMA is used; the stream is bound by
+// HBM bandwidth, with VALU/exp issue close behind for bfloat16 stochastic rows.
+//
+// Two layouts (see sv_internal.h): sequence-resident (one workgroup streams a
+// whole sequence; nothing crosses workgroups) and row-split (a statistics
+// kernel over (row, slice) items, then a finishing kernel per sequence).
 //
 // The method (Perplexity, "Accelerating Sonar through speculation", sections
 // "Špekulatívne dekódovanie" and "Cieľ-Návrh"): compare complete target and
@@ -28,95 +32,24 @@
 
 namespace sv {
 
-constexpr int NT = 256;        // threads per workgroup: four wave64s
-constexpr int NW = NT / 64;    // waves per workgroup
-constexpr int UNROLL = 8;      // 16-byte loads in flight per lane (stream)
-constexpr int TUNROLL = 4;     // row pairs in flight per lane (tail)
+constexpr int NT_SEQ = 1024;   // sequence-resident workgroup: 16 wave64s
+constexpr int NT_ROW = 256;    // row-split statistics workgroup: 4 wave64s
+constexpr int NT_FIN = 1024;   // row-split finishing workgroup
+constexpr int UNROLL = 8;      // 16-byte loads in flight per lane while streaming
+constexpr int TUNROLL = 4;     // chunk pairs in flight per lane while sampling
 constexpr int MAX_TILES = 256; // inverse-CDF tiles held in LDS
-// How far (in log2 units) the streaming reference may sit below a new
-// maximum before the running sum is rescaled.  Terms then stay <= 2^16.
+constexpr int MAX_ROWS_STOCH = 2 * kMaxK + 1;
+constexpr int MAX_ROWS_GREEDY_SEQ = kMaxK + 1;
+// How far (log2 units) a new maximum may exceed the streaming reference
+// before the running sum is rescaled; terms then stay below 2^16.
 constexpr float RESCALE_MARGIN = 16.0f;
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-class parts.
+constexpr int RSRC_WORD3 = 0x00020000;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ------------------------------------------------------------------------
-// Element access.  DT 0 = float32, 1 = bfloat16.  VEC: 16-byte chunks
-// (8 bf16 or 4 f32), else one element per load.
-template <int DT, bool VEC>
-struct Chunk;
-
-template <>
-struct Chunk<1, true> {
-    static constexpr int E = 8;
-    uint4 w;
-    __device__ __forceinline__ static Chunk load(const char* row, int i) {
-        Chunk c;
-        c.w = reinterpret_cast<const uint4*>(row)[i];
-        return c;
-    }
-    __device__ __forceinline__ static Chunk neg_inf() {
-        Chunk c;
-        c.w = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-        return c;
-    }
-    __device__ __forceinline__ float get(int j) const {
-        uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
-        return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
-    }
-};
-
-template <>
-struct Chunk<0, true> {
-    static constexpr int E = 4;
-    float4 w;
-    __device__ __forceinline__ static Chunk load(const char* row, int i) {
-        Chunk c;
-        c.w = reinterpret_cast<const float4*>(row)[i];
-        return c;
-    }
-    __device__ __forceinline__ static Chunk neg_inf() {
-        Chunk c;
-        c.w = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        return c;
-    }
-    __device__ __forceinline__ float get(int j) const {
-        return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w;
-    }
-};
-
-template <>
-struct Chunk<1, false> {
-    static constexpr int E = 1;
-    uint32_t w;
-    __device__ __forceinline__ static Chunk load(const char* row, int i) {
-        Chunk c;
-        c.w = (uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16;
-        return c;
-    }
-    __device__ __forceinline__ static Chunk neg_inf() {
-        Chunk c;
-        c.w = 0xff800000u;
-        return c;
-    }
-    __device__ __forceinline__ float get(int) const { return __uint_as_float(w); }
-};
-
-template <>
-struct Chunk<0, false> {
-    static constexpr int E = 1;
-    float w;
-    __device__ __forceinline__ static Chunk load(const char* row, int i) {
-        Chunk c;
-        c.w = reinterpret_cast<const float*>(row)[i];
-        return c;
-    }
-    __device__ __forceinline__ static Chunk neg_inf() {
-        Chunk c;
-        c.w = -INFINITY;
-        return c;
-    }
-    __device__ __forceinline__ float get(int) const { return w; }
-};
+template <int DT>
+constexpr int elem_bytes() { return DT == 1 ? 2 : 4; }
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const char* row, int v) {
@@ -124,11 +57,98 @@ __device__ __forceinline__ float load_elem(const char* row, int v) {
     return reinterpret_cast<const float*>(row)[v];
 }
 
+// ------------------------------------------------------------------------
+// Chunks: E consecutive logits.  VEC: 16 bytes (8 bf16 or 4 f32), else one.
+template <int DT, bool VEC>
+struct Chunk;
+
+template <>
+struct Chunk<1, true> {
+    static constexpr int E = 8;
+    uint32_t w[4];
+    __device__ __forceinline__ float get(int j) const {
+        const uint32_t x = w[j >> 1];
+        return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+    }
+    __device__ __forceinline__ void set_neg_inf() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = 0xff80ff80u;
+    }
+};
+
+template <>
+struct Chunk<0, true> {
+    static constexpr int E = 4;
+    uint32_t w[4];
+    __device__ __forceinline__ float get(int j) const { return __uint_as_float(w[j]); }
+    __device__ __forceinline__ void set_neg_inf() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = 0xff800000u;
+    }
+};
+
 template <int DT>
-constexpr int elem_bytes() { return DT == 1 ? 2 : 4; }
+struct Chunk1 {
+    static constexpr int E = 1;
+    uint32_t w[1];
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(w[0]); }
+    __device__ __forceinline__ void set_neg_inf() { w[0] = 0xff800000u; }
+};
+template <>
+struct Chunk<1, false> : Chunk1<1> {};
+template <>
+struct Chunk<0, false> : Chunk1<0> {};
+
+// n logits at `base` (a row or a slice of one).  VEC rows start on a
+// 16-byte boundary and are read through a buffer resource that covers
+// exactly their whole chunks, so an index can never leave the row; the
+// n % E trailing logits are read one by one.  chunk_at(i, s) is chunk i + s
+// with s uniform across the wave (folded into the scalar offset).
+template <int DT, bool VEC>
+struct Row;
+
+template <int DT>
+struct Row<DT, true> {
+    using C = Chunk<DT, true>;
+    static constexpr int E = C::E;
+    __amdgpu_buffer_rsrc_t rs;
+    const char* base;
+    int n, nch;
+    __device__ __forceinline__ Row(const char* p, int n_) : base(p), n(n_), nch(n_ / E) {
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, nch * 16,
+                                               RSRC_WORD3);
+    }
+    __device__ __forceinline__ C chunk_at(int i, int s) const {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, s * 16, 0);
+        C c;
+        c.w[0] = v[0];
+        c.w[1] = v[1];
+        c.w[2] = v[2];
+        c.w[3] = v[3];
+        return c;
+    }
+    __device__ __forceinline__ C chunk(int i) const { return chunk_at(i, 0); }
+    __device__ __forceinline__ float elem(int v) const { return load_elem<DT>(base, v); }
+};
+
+template <int DT>
+struct Row<DT, false> {
+    using C = Chunk<DT, false>;
+    static constexpr int E = 1;
+    const char* base;
+    int n, nch;
+    __device__ __forceinline__ Row(const char* p, int n_) : base(p), n(n_), nch(n_) {}
+    __device__ __forceinline__ C chunk_at(int i, int s) const {
+        C c;
+        c.w[0] = __float_as_uint(load_elem<DT>(base, i + s));
+        return c;
+    }
+    __device__ __forceinline__ C chunk(int i) const { return chunk_at(i, 0); }
+    __device__ __forceinline__ float elem(int v) const { return load_elem<DT>(base, v); }
+};
 
 // ------------------------------------------------------------------------
-// Wave / block reductions (wave64).
+// Wave64 and block reductions.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -149,29 +169,46 @@ __device__ __forceinline__ int wave_max_i(int v) {
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
     return v;
 }
-// Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_incl_scan(float v) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        float n = __shfl_up(v, o);
+        const float n = __shfl_up(v, o);
         if (lane >= o) v += n;
     }
     return v;
 }
+// Larger value wins; equal values go to the lower index.
+__device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+__device__ __forceinline__ void wave_argmax(float& best, int& idx) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o);
+        const int oi = __shfl_xor(idx, o);
+        if (argmax_better(ob, oi, best, idx)) {
+            best = ob;
+            idx = oi;
+        }
+    }
+}
 
-struct BlockScratch {
+template <int NT>
+struct Scratch {
+    static constexpr int NW = NT / 64;
     float f[NW];
     float g[NW];
     int i[NW];
     int j[NW];
 };
 
-// Block-wide exclusive prefix sum; *total receives the block sum.  All
-// threads must call.
-__device__ __forceinline__ float block_excl_scan(float v, float* total, BlockScratch& sc) {
+// Block-wide exclusive prefix sum; *total gets the block sum.  All threads call.
+template <int NT>
+__device__ __forceinline__ float block_excl_scan(float v, float* total, Scratch<NT>& sc) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float incl = wave_incl_scan(v);
+    const float incl = wave_incl_scan(v);
     float excl = __shfl_up(incl, 1);
     if (lane == 0) excl = 0.0f;
     if (lane == 63) sc.f[wave] = incl;
@@ -187,7 +224,9 @@ __device__ __forceinline__ float block_excl_scan(float v, float* total, BlockScr
     return off + excl;
 }
 
-__device__ __forceinline__ int block_min_i(int v, BlockScratch& sc) {
+template <int NT>
+__device__ __forceinline__ int block_min_i(int v, Scratch<NT>& sc) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_min_i(v);
     if (lane == 0) sc.i[wave] = v;
@@ -199,7 +238,9 @@ __device__ __forceinline__ int block_min_i(int v, BlockScratch& sc) {
     return r;
 }
 
-__device__ __forceinline__ int block_max_i(int v, BlockScratch& sc) {
+template <int NT>
+__device__ __forceinline__ int block_max_i(int v, Scratch<NT>& sc) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_max_i(v);
     if (lane == 0) sc.j[wave] = v;
@@ -212,231 +253,143 @@ __device__ __forceinline__ int block_max_i(int v, BlockScratch& sc) {
 }
 
 // ------------------------------------------------------------------------
-// Streaming pass, stochastic: (R, Z) of elements [v0, v1) of one row with
-// Z = sum 2^(x*c - R).  Result valid in thread 0.
-template <int DT, bool VEC>
-__device__ __forceinline__ void stream_softmax_stats(const char* row, int v0, int v1, float c,
-                                                     float* R_out, float* Z_out, BlockScratch& sc) {
+// Streaming reductions of one row, per thread.  Thread t visits chunks
+// t, t+NT, t+2NT, ... in increasing order, UNROLL loads in flight.
+
+// Softmax normaliser of one thread: sum (s0 + s1) of 2^(x*c - ref).
+struct SoftAcc {
+    float ref = -FLT_MAX, s0 = 0.0f, s1 = 0.0f;
+};
+
+__device__ __forceinline__ void soft_rescale(SoftAcc& a, float newref) {
+    const float f = fast_exp2(a.ref - newref);
+    a.s0 *= f;
+    a.s1 *= f;
+    a.ref = newref;
+}
+
+template <typename C>
+__device__ __forceinline__ void soft_consume(const C* buf, float c, SoftAcc& a) {
+    constexpr int E = C::E;
+    float gm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) gm = fmaxf(gm, buf[u].get(e));
+    const float gmc = gm * c;
+    if (gmc > a.ref + RESCALE_MARGIN) soft_rescale(a, gmc);
+    const float nref = -a.ref;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float t = fast_exp2(fmaf(buf[u].get(e), c, nref));
+            if (e & 1) a.s1 += t;
+            else a.s0 += t;
+        }
+}
+
+template <int DT, bool VEC, int NT>
+__device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c, SoftAcc& a) {
     using C = Chunk<DT, VEC>;
     constexpr int E = C::E;
-    const char* base = row + (size_t)v0 * elem_bytes<DT>();
-    const int n = v1 - v0;
-    const int nch = n / E;
+    constexpr int STEP = NT * UNROLL;
     const int tid = threadIdx.x;
-    float ref = -FLT_MAX, s0 = 0.0f, s1 = 0.0f;
-
-    auto consume = [&](const C* buf, int cnt) {
-        float gm = -INFINITY;
+    const int nch = row.nch;
+    for (int i0 = 0; i0 < nch; i0 += STEP) {
+        const int i = i0 + tid;
+        C buf[UNROLL];
+        if (i0 + STEP <= nch) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            if (u < cnt) {
+            for (int u = 0; u < UNROLL; ++u) buf[u] = row.chunk_at(i, u * NT);
+        } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) gm = fmaxf(gm, buf[u].get(e));
+            for (int u = 0; u < UNROLL; ++u) {
+                if (i + u * NT < nch) buf[u] = row.chunk_at(i, u * NT);
+                else buf[u].set_neg_inf();
             }
         }
-        const float gmc = gm * c;
-        if (gmc > ref + RESCALE_MARGIN) {
-            const float sc_ = fast_exp2(ref - gmc);
-            s0 *= sc_;
-            s1 *= sc_;
-            ref = gmc;
-        }
-        const float nref = -ref;
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            if (u < cnt) {
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float t = fast_exp2(fmaf(buf[u].get(e), c, nref));
-                    if (e & 1) s1 += t;
-                    else s0 += t;
-                }
-            }
-        }
-    };
-
-    const int step = NT * UNROLL;
-    const int full_end = (nch / step) * step;
-    for (int i = tid; i < full_end; i += step) {
-        C buf[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) buf[u] = C::load(base, i + u * NT);
-        consume(buf, UNROLL);
+        soft_consume(buf, c, a);
     }
-    if (full_end < nch) {
-        C buf[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int idx = full_end + tid + u * NT;
-            buf[u] = idx < nch ? C::load(base, idx) : C::neg_inf();
-        }
-        consume(buf, UNROLL);
-    }
-    // Elements past the last whole chunk (vector path only).
     if (VEC) {
-        const int rem = n - nch * E;
+        const int rem = row.n - nch * E;
         if (tid < rem) {
-            const float x = load_elem<DT>(base, nch * E + tid);
-            const float xc = x * c;
-            if (xc > ref + RESCALE_MARGIN) {
-                const float sc_ = fast_exp2(ref - xc);
-                s0 *= sc_;
-                s1 *= sc_;
-                ref = xc;
-            }
-            s0 += fast_exp2(fmaf(x, c, -ref));
+            const float x = row.elem(nch * E + tid);
+            if (x * c > a.ref + RESCALE_MARGIN) soft_rescale(a, x * c);
+            a.s0 += fast_exp2(fmaf(x, c, -a.ref));
         }
-    }
-    // Merge (ref, sum) across the block.
-    const int lane = tid & 63, wave = tid >> 6;
-    float R = wave_max(ref);
-    float S = wave_sum((s0 + s1) * fast_exp2(ref - R));
-    if (lane == 0) {
-        sc.f[wave] = R;
-        sc.g[wave] = S;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float RR = sc.f[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) RR = fmaxf(RR, sc.f[w]);
-        float SS = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) SS += sc.g[w] * fast_exp2(sc.f[w] - RR);
-        *R_out = RR;
-        *Z_out = SS;
     }
 }
 
-// Streaming pass, greedy: maximum of elements [v0, v1) and the lowest
-// (absolute) index holding it.  Result valid in thread 0.
-template <int DT, bool VEC>
-__device__ __forceinline__ void stream_argmax(const char* row, int v0, int v1, float* M_out,
-                                              int* I_out, BlockScratch& sc) {
+// Merge a wave's softmax normalisers into (R, Z) (valid in every lane).
+__device__ __forceinline__ void wave_softmax(const SoftAcc& a, float& R, float& Z) {
+    R = wave_max(a.ref);
+    Z = wave_sum((a.s0 + a.s1) * fast_exp2(a.ref - R));
+}
+
+// Argmax of one thread: best value and the element index where a chunk
+// holding it starts (or of a single trailing element).
+struct ArgAcc {
+    float best = -INFINITY;
+    int pos = INT_MAX;
+};
+
+template <int DT, bool VEC, int NT>
+__device__ __forceinline__ void stream_argmax(const Row<DT, VEC>& row, ArgAcc& a) {
     using C = Chunk<DT, VEC>;
     constexpr int E = C::E;
-    const char* base = row + (size_t)v0 * elem_bytes<DT>();
-    const int n = v1 - v0;
-    const int nch = n / E;
-    const int rem = VEC ? n - nch * E : 0;
+    constexpr int STEP = NT * UNROLL;
     const int tid = threadIdx.x;
-    // best: this thread's maximum; bpos: element offset (from v0) of the
-    // chunk that first reached it, or of a single trailing element when
-    // bpos >= nch*E.
-    float best = -INFINITY;
-    int bpos = tid < nch ? tid * E : (tid < rem ? nch * E + tid : INT_MAX);
-
-    const int step = NT * UNROLL;
-    const int full_end = (nch / step) * step;
-    for (int i = tid; i < full_end; i += step) {
+    const int nch = row.nch;
+    const int rem = VEC ? row.n - nch * E : 0;
+    // An all -inf row still has an argmax: the thread's first element.
+    a.pos = tid < nch ? tid * E : (tid < rem ? nch * E + tid : INT_MAX);
+    for (int i0 = 0; i0 < nch; i0 += STEP) {
+        const int i = i0 + tid;
         C buf[UNROLL];
+        if (i0 + STEP <= nch) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) buf[u] = C::load(base, i + u * NT);
+            for (int u = 0; u < UNROLL; ++u) buf[u] = row.chunk_at(i, u * NT);
+        } else {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            float m = buf[u].get(0);
-#pragma unroll
-            for (int e = 1; e < E; ++e) m = fmaxf(m, buf[u].get(e));
-            if (m > best) {
-                best = m;
-                bpos = (i + u * NT) * E;
+            for (int u = 0; u < UNROLL; ++u) {
+                if (i + u * NT < nch) buf[u] = row.chunk_at(i, u * NT);
+                else buf[u].set_neg_inf();
             }
         }
-    }
-    if (full_end < nch) {
-        C buf[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int idx = full_end + tid + u * NT;
-            buf[u] = idx < nch ? C::load(base, idx) : C::neg_inf();
-        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             float m = buf[u].get(0);
 #pragma unroll
             for (int e = 1; e < E; ++e) m = fmaxf(m, buf[u].get(e));
-            if (m > best) {
-                best = m;
-                bpos = (full_end + tid + u * NT) * E;
+            if (m > a.best) {
+                a.best = m;
+                a.pos = (i + u * NT) * E;
             }
         }
     }
     if (VEC && tid < rem) {
-        const float x = load_elem<DT>(base, nch * E + tid);
-        if (x > best) {
-            best = x;
-            bpos = nch * E + tid;
+        const float x = row.elem(nch * E + tid);
+        if (x > a.best) {
+            a.best = x;
+            a.pos = nch * E + tid;
         }
-    }
-    // Lowest index inside the winning chunk.
-    int idx = INT_MAX;
-    if (bpos < nch * E) {
-        const C ch = C::load(base, bpos / E);
-#pragma unroll
-        for (int e = E - 1; e >= 0; --e)
-            if (ch.get(e) == best) idx = bpos + e;
-    } else if (bpos != INT_MAX) {
-        idx = bpos;
-    }
-    // Block argmax: larger value wins, lower index on equal values.
-    const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ob = __shfl_xor(best, o);
-        const int oi = __shfl_xor(idx, o);
-        if (ob > best || (ob == best && oi < idx)) {
-            best = ob;
-            idx = oi;
-        }
-    }
-    if (lane == 0) {
-        sc.f[wave] = best;
-        sc.i[wave] = idx;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float bb = sc.f[0];
-        int ii = sc.i[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w)
-            if (sc.f[w] > bb || (sc.f[w] == bb && sc.i[w] < ii)) {
-                bb = sc.f[w];
-                ii = sc.i[w];
-            }
-        *M_out = bb;
-        *I_out = ii == INT_MAX ? v0 : v0 + ii;
     }
 }
 
-// ------------------------------------------------------------------------
-// Arrival: thread 0 publishes this workgroup's statistics and counts in; the
-// workgroup that completes its sequence returns true (in every thread).
-__device__ __forceinline__ bool arrive(const Params& p, int b, int item, float a, float bv,
-                                       int* flag) {
-    const int per_seq = p.rows_per_seq * p.S;
-    if (threadIdx.x == 0) {
-        float* dst = p.part + ((size_t)b * per_seq + item) * 2;
-        dst[0] = a;
-        dst[1] = bv;
-        __threadfence();
-        const int old = atomicAdd(&p.counters[b], 1);
-        *flag = (old == per_seq - 1);
-        if (*flag) __threadfence();
-    }
-    __syncthreads();
-    const bool last = *flag != 0;
-    if (last) __threadfence();
-    return last;
-}
-
-// The finishing workgroup has read its sequence's statistics; zero them so
-// the whole workspace is zero again when the call completes (the counter is
-// reset separately).  A later call with another shape may place its counters
-// where these statistics were.
-__device__ __forceinline__ void clear_partials(const Params& p, int b) {
-    const int n = p.rows_per_seq * p.S * 2;
-    float* dst = p.part + (size_t)b * n;
-    for (int j = threadIdx.x; j < n; j += NT) dst[j] = 0.0f;
+// Lowest index holding `best`, given the lowest chunk (start `pos`) that
+// holds it.
+template <int DT, bool VEC>
+__device__ __forceinline__ int argmax_refine(const Row<DT, VEC>& row, float best, int pos) {
+    using C = Chunk<DT, VEC>;
+    constexpr int E = C::E;
+    if (pos >= row.nch * E) return pos == INT_MAX ? 0 : pos;
+    const C ch = row.chunk(pos / E);
+    int idx = pos;
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e)
+        if (ch.get(e) == best) idx = pos + e;
+    return idx;
 }
 
 // ------------------------------------------------------------------------
@@ -445,25 +398,28 @@ __device__ __forceinline__ void clear_partials(const Params& p, int b) {
 // leaves none, the last index with positive weight (0 if there is none).
 // The row is cut into tiles of NT*m chunks; pass A sums each tile, a block
 // scan over tile sums finds the tile holding the draw, pass B scans inside
-// that tile.  *total receives the total weight.  All threads must call.
-template <int DT, bool VEC, bool PAIR, typename W>
-__device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const W& wf, float r,
+// that tile.  *total gets the total weight.  All threads call.
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+__device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const Wt& wf, float r,
                                float* total_out, float* tile_part, float* tile_excl,
-                               BlockScratch& sc) {
+                               Scratch<NT>& sc) {
     using C = Chunk<DT, VEC>;
     constexpr int E = C::E;
+    constexpr int NW = NT / 64;
+    const Row<DT, VEC> tr(trow, V);
+    const Row<DT, VEC> dr(PAIR ? drow : trow, V);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nch = V / E;
+    const int nch = tr.nch;
     const int rem = VEC ? V - nch * E : 0;
-    const int rounds = (nch + NT - 1) / NT;         // block-wide rounds of chunks
+    const int rounds = (nch + NT - 1) / NT;                      // block-wide rounds of chunks
     const int m = max(1, (rounds + MAX_TILES - 1) / MAX_TILES);  // rounds per tile
     const int ntiles = (rounds + m - 1) / m;
-    const int nt_all = ntiles + (rem > 0 ? 1 : 0);  // trailing elements = last tile
+    const int nt_all = ntiles + (rem > 0 ? 1 : 0);               // trailing logits = last tile
 
     for (int t = tid; t < nt_all * NW; t += NT) tile_part[t] = 0.0f;
     __syncthreads();
 
-    // Pass A: per-tile partial sums, per wave.
+    // Pass A: per-tile partial sums, one slot per wave.
     int lastpos = -1;
     for (int r0 = 0; r0 < rounds; r0 += TUNROLL) {
         C tb[TUNROLL], db[TUNROLL];
@@ -471,11 +427,11 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
         for (int u = 0; u < TUNROLL; ++u) {
             const int ci = (r0 + u) * NT + tid;
             if (ci < nch) {
-                tb[u] = C::load(trow, ci);
-                if (PAIR) db[u] = C::load(drow, ci);
+                tb[u] = tr.chunk(ci);
+                if (PAIR) db[u] = dr.chunk(ci);
             } else {
-                tb[u] = C::neg_inf();
-                if (PAIR) db[u] = C::neg_inf();
+                tb[u].set_neg_inf();
+                if (PAIR) db[u].set_neg_inf();
             }
         }
 #pragma unroll
@@ -498,8 +454,8 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
     if (rem > 0) {
         float w = 0.0f;
         if (tid < rem) {
-            const float tv = load_elem<DT>(trow, nch * E + tid);
-            const float dv = PAIR ? load_elem<DT>(drow, nch * E + tid) : 0.0f;
+            const float tv = tr.elem(nch * E + tid);
+            const float dv = PAIR ? dr.elem(nch * E + tid) : 0.0f;
             w = wf(tv, dv);
             if (w > 0.0f) lastpos = nch * E + tid;
         }
@@ -523,7 +479,7 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
         run += s;
     }
     float total;
-    const float excl = block_excl_scan(run, &total, sc);
+    const float excl = block_excl_scan<NT>(run, &total, sc);
     const float T = r * total;
     int cross = INT_MAX;
     {
@@ -537,36 +493,35 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
             }
         }
     }
-    cross = block_min_i(cross, sc);  // barrier also publishes tile_excl
+    cross = block_min_i<NT>(cross, sc);  // its barrier also publishes tile_excl
     *total_out = total;
-
-    if (cross == INT_MAX) return max(block_max_i(lastpos, sc), 0);
+    if (cross == INT_MAX) return max(block_max_i<NT>(lastpos, sc), 0);
 
     // Pass B: scan inside the crossing tile.
     float cum = tile_excl[cross];
     int found = INT_MAX;
     int tile_last = -1;
-    if (cross == ntiles) {  // the trailing-elements tile
+    if (cross == ntiles) {  // the trailing-logits tile
         float w = 0.0f;
         if (tid < rem) {
-            const float tv = load_elem<DT>(trow, nch * E + tid);
-            const float dv = PAIR ? load_elem<DT>(drow, nch * E + tid) : 0.0f;
+            const float tv = tr.elem(nch * E + tid);
+            const float dv = PAIR ? dr.elem(nch * E + tid) : 0.0f;
             w = wf(tv, dv);
             if (w > 0.0f) tile_last = nch * E + tid;
         }
         float tot;
-        const float ex = block_excl_scan(w, &tot, sc);
+        const float ex = block_excl_scan<NT>(w, &tot, sc);
         if (w > 0.0f && cum + (ex + w) > T) found = nch * E + tid;
-        found = block_min_i(found, sc);
+        found = block_min_i<NT>(found, sc);
     } else {
         for (int rd = cross * m; rd < min(rounds, (cross + 1) * m); ++rd) {
             const int ci = rd * NT + tid;
             float wv[E];
             float loc = 0.0f;
             if (ci < nch) {
-                const C tc = C::load(trow, ci);
+                const C tc = tr.chunk(ci);
                 C dc;
-                if (PAIR) dc = C::load(drow, ci);
+                if (PAIR) dc = dr.chunk(ci);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     wv[e] = PAIR ? wf(tc.get(e), dc.get(e)) : wf(tc.get(e), 0.0f);
@@ -578,7 +533,7 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
                 for (int e = 0; e < E; ++e) wv[e] = 0.0f;
             }
             float tot;
-            const float ex = block_excl_scan(loc, &tot, sc);
+            const float ex = block_excl_scan<NT>(loc, &tot, sc);
             int f = INT_MAX;
             float run_e = ex;
 #pragma unroll
@@ -586,13 +541,13 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
                 run_e += wv[e];
                 if (f == INT_MAX && wv[e] > 0.0f && cum + run_e > T) f = ci * E + e;
             }
-            found = block_min_i(f, sc);
-            if (found != INT_MAX) break;
+            found = block_min_i<NT>(f, sc);
+            if (found != INT_MAX) break;  // uniform
             cum += tot;
         }
     }
     if (found != INT_MAX) return found;
-    return max(block_max_i(tile_last, sc), 0);
+    return max(block_max_i<NT>(tile_last, sc), 0);
 }
 
 // Residual weight max(0, p - q) of one row pair.
@@ -613,19 +568,7 @@ struct TargetW {
 };
 
 // ------------------------------------------------------------------------
-constexpr int MAX_ROWS_STOCH = 2 * kMaxK + 1;
-
-struct StochSmem {
-    BlockScratch sc;
-    int flag;
-    int a;
-    float R[MAX_ROWS_STOCH];
-    float Z[MAX_ROWS_STOCH];
-    float px[kMaxK];
-    float qx[kMaxK];
-    float tile_part[(MAX_TILES + 1) * NW];
-    float tile_excl[MAX_TILES + 1];
-};
+// Finishing a sequence.
 
 template <int DT>
 __device__ __forceinline__ const char* stoch_row(const Params& p, int b, int r) {
@@ -637,36 +580,29 @@ __device__ __forceinline__ const char* stoch_row(const Params& p, int b, int r) 
            ((size_t)b * p.k + (r - p.k - 1)) * (size_t)p.row_stride * eb;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT) void k_verify_stochastic(Params p) {
-    __shared__ StochSmem sm;
-    const int per_seq = p.rows_per_seq * p.S;
-    const int b = blockIdx.x / per_seq;
-    const int item = blockIdx.x - b * per_seq;
-    const int r = item / p.S;
-    const int s = item - r * p.S;
-    const int v0 = s * p.slice_len;
-    const int v1 = min(p.V, v0 + p.slice_len);
+template <int DT>
+__device__ __forceinline__ const char* greedy_row(const Params& p, int b, int r) {
+    return static_cast<const char*>(p.target) +
+           ((size_t)b * p.rows_per_seq + r) * (size_t)p.row_stride * elem_bytes<DT>();
+}
 
-    float R = 0.0f, Z = 0.0f;
-    stream_softmax_stats<DT, VEC>(stoch_row<DT>(p, b, r), v0, v1, p.c, &R, &Z, sm.sc);
-    if (!arrive(p, b, item, R, Z, &sm.flag)) return;
+template <int NT>
+struct StochFin {
+    Scratch<NT> sc;
+    int a;
+    float R[MAX_ROWS_STOCH];  // rows 0..k: target, k+1..2k: draft
+    float Z[MAX_ROWS_STOCH];
+    float px[kMaxK];
+    float qx[kMaxK];
+    float tile_part[(MAX_TILES + 1) * (NT / 64)];
+    float tile_excl[MAX_TILES + 1];
+};
 
-    // ---- last workgroup of sequence b ----
+// Needs R[], Z[] of every row of sequence b in LDS (after a barrier).
+template <int DT, bool VEC, int NT>
+__device__ void finish_stochastic(const Params& p, int b, StochFin<NT>& sm) {
     const int tid = threadIdx.x;
     const int k = p.k, V = p.V;
-    const float* part = p.part + (size_t)b * per_seq * 2;
-    for (int row = tid; row < p.rows_per_seq; row += NT) {
-        float RR = -FLT_MAX;
-        for (int j = 0; j < p.S; ++j) RR = fmaxf(RR, part[(row * p.S + j) * 2]);
-        float ZZ = 0.0f;
-        for (int j = 0; j < p.S; ++j)
-            ZZ += part[(row * p.S + j) * 2 + 1] * fast_exp2(part[(row * p.S + j) * 2] - RR);
-        sm.R[row] = RR;
-        sm.Z[row] = ZZ;
-    }
-    __syncthreads();
-    clear_partials(p, b);
     const int32_t* x = p.tokens_in + (size_t)b * k;
     for (int i = tid; i < k; i += NT) {
         const int xi = x[i];
@@ -708,73 +644,40 @@ __global__ __launch_bounds__(NT) void k_verify_stochastic(Params p) {
     int y;
     if (a < k) {
         const char* drow = stoch_row<DT>(p, b, k + 1 + a);
-        ResidualW w{p.c, -sm.R[a], 1.0f / sm.Z[a], -sm.R[k + 1 + a], 1.0f / sm.Z[k + 1 + a]};
-        y = inverse_cdf_row<DT, VEC, true>(trow, drow, V, w, rr, &total, sm.tile_part,
-                                           sm.tile_excl, sm.sc);
+        const ResidualW w{p.c, -sm.R[a], 1.0f / sm.Z[a], -sm.R[k + 1 + a], 1.0f / sm.Z[k + 1 + a]};
+        y = inverse_cdf_row<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.tile_part,
+                                               sm.tile_excl, sm.sc);
         if (!(total > 0.0f)) {
             // p == q to float precision: the residual is empty; draw from p_a.
-            TargetW tw{p.c, -sm.R[a]};
-            y = inverse_cdf_row<DT, VEC, false>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
-                                                sm.tile_excl, sm.sc);
+            const TargetW tw{p.c, -sm.R[a]};
+            y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
+                                                    sm.tile_excl, sm.sc);
         }
     } else {
-        TargetW tw{p.c, -sm.R[k]};
-        y = inverse_cdf_row<DT, VEC, false>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
-                                            sm.tile_excl, sm.sc);
+        const TargetW tw{p.c, -sm.R[k]};
+        y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
+                                                sm.tile_excl, sm.sc);
     }
     if (tid == 0) {
         out[a] = y;
         p.accept_len[b] = a;
-        p.counters[b] = 0;  // leave the workspace zeroed for the next call
     }
 }
 
-// ------------------------------------------------------------------------
-struct GreedySmem {
-    BlockScratch sc;
-    int flag;
+template <int NT>
+struct GreedyFin {
+    Scratch<NT> sc;
     int a;
     int c;
-    int g[kMaxRowsPerSeq];
+    int g[kMaxRowsPerSeq];           // argmax of every row of the sequence
     int cand_a[kMaxRowsPerSeq / 2];  // G <= kMaxRowsPerSeq / (k+1), k >= 1
 };
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT) void k_verify_greedy(Params p) {
-    __shared__ GreedySmem sm;
-    const int per_seq = p.rows_per_seq * p.S;
-    const int b = blockIdx.x / per_seq;
-    const int item = blockIdx.x - b * per_seq;
-    const int r = item / p.S;
-    const int s = item - r * p.S;
-    const int v0 = s * p.slice_len;
-    const int v1 = min(p.V, v0 + p.slice_len);
-    const char* row = static_cast<const char*>(p.target) +
-                      ((size_t)b * p.rows_per_seq + r) * (size_t)p.row_stride * elem_bytes<DT>();
-
-    float M = 0.0f;
-    int I = 0;
-    stream_argmax<DT, VEC>(row, v0, v1, &M, &I, sm.sc);
-    if (!arrive(p, b, item, M, __int_as_float(I), &sm.flag)) return;
-
-    // ---- last workgroup of sequence b ----
+// Needs g[] of every row of sequence b in LDS (after a barrier).
+template <int NT>
+__device__ void finish_greedy(const Params& p, int b, GreedyFin<NT>& sm) {
     const int tid = threadIdx.x;
     const int k = p.k, G = p.G;
-    const float* part = p.part + (size_t)b * per_seq * 2;
-    for (int rw = tid; rw < p.rows_per_seq; rw += NT) {
-        float bm = part[(rw * p.S) * 2];
-        int bi = __float_as_int(part[(rw * p.S) * 2 + 1]);
-        for (int j = 1; j < p.S; ++j) {
-            const float mj = part[(rw * p.S + j) * 2];
-            if (mj > bm) {  // earlier slices win ties: lowest index
-                bm = mj;
-                bi = __float_as_int(part[(rw * p.S + j) * 2 + 1]);
-            }
-        }
-        sm.g[rw] = bi;
-    }
-    __syncthreads();
-    clear_partials(p, b);
     const int32_t* x = p.tokens_in + (size_t)b * G * k;
     for (int c = tid; c < G; c += NT) {
         int a = k;
@@ -789,7 +692,7 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(Params p) {
     if (tid == 0) {
         int bc = 0, ba = sm.cand_a[0];
         for (int c = 1; c < G; ++c)
-            if (sm.cand_a[c] > ba) {
+            if (sm.cand_a[c] > ba) {  // lowest candidate wins ties
                 ba = sm.cand_a[c];
                 bc = c;
             }
@@ -797,7 +700,6 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(Params p) {
         sm.c = bc;
         p.accept_len[b] = ba;
         if (p.best_cand) p.best_cand[b] = bc;
-        p.counters[b] = 0;
     }
     __syncthreads();
     const int a = sm.a, bc = sm.c;
@@ -806,29 +708,234 @@ __global__ __launch_bounds__(NT) void k_verify_greedy(Params p) {
 }
 
 // ------------------------------------------------------------------------
+// Sequence-resident kernels: one workgroup per sequence.
+
+struct StochSeqSmem {
+    StochFin<NT_SEQ> fin;
+    float wR[MAX_ROWS_STOCH * (NT_SEQ / 64)];  // per-wave partial normalisers
+    float wZ[MAX_ROWS_STOCH * (NT_SEQ / 64)];
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
+    constexpr int NW = NT_SEQ / 64;
+    __shared__ StochSeqSmem sm;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int k = p.k;
+    const int rows = 2 * k + 1;
+    // Target row k first, then the pairs from position k-1 down to 0, so the
+    // rows a rejection most often lands on are the freshest in cache when
+    // the residual draw reads them again.
+    for (int j = 0; j < rows; ++j) {
+        const int i = k - (j + 1) / 2;
+        const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
+        const Row<DT, VEC> row(stoch_row<DT>(p, b, r), p.V);
+        SoftAcc acc;
+        stream_softmax<DT, VEC, NT_SEQ>(row, p.c, acc);
+        float R, Z;
+        wave_softmax(acc, R, Z);
+        if (lane == 0) {
+            sm.wR[r * NW + wave] = R;
+            sm.wZ[r * NW + wave] = Z;
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < rows; r += NT_SEQ) {
+        float R = sm.wR[r * NW];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) R = fmaxf(R, sm.wR[r * NW + w]);
+        float Z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) Z += sm.wZ[r * NW + w] * fast_exp2(sm.wR[r * NW + w] - R);
+        sm.fin.R[r] = R;
+        sm.fin.Z[r] = Z;
+    }
+    __syncthreads();
+    finish_stochastic<DT, VEC, NT_SEQ>(p, b, sm.fin);
+}
+
+struct GreedySeqSmem {
+    GreedyFin<NT_SEQ> fin;
+    float wbest[MAX_ROWS_GREEDY_SEQ * (NT_SEQ / 64)];
+    int wpos[MAX_ROWS_GREEDY_SEQ * (NT_SEQ / 64)];
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
+    constexpr int NW = NT_SEQ / 64;
+    __shared__ GreedySeqSmem sm;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rows = p.rows_per_seq;  // k+1 (one candidate)
+    for (int r = 0; r < rows; ++r) {
+        const Row<DT, VEC> row(greedy_row<DT>(p, b, r), p.V);
+        ArgAcc acc;
+        stream_argmax<DT, VEC, NT_SEQ>(row, acc);
+        wave_argmax(acc.best, acc.pos);
+        if (lane == 0) {
+            sm.wbest[r * NW + wave] = acc.best;
+            sm.wpos[r * NW + wave] = acc.pos;
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < rows; r += NT_SEQ) {
+        float best = sm.wbest[r * NW];
+        int pos = sm.wpos[r * NW];
+        for (int w = 1; w < NW; ++w)
+            if (argmax_better(sm.wbest[r * NW + w], sm.wpos[r * NW + w], best, pos)) {
+                best = sm.wbest[r * NW + w];
+                pos = sm.wpos[r * NW + w];
+            }
+        const Row<DT, VEC> row(greedy_row<DT>(p, b, r), p.V);
+        sm.fin.g[r] = argmax_refine(row, best, pos);
+    }
+    __syncthreads();
+    finish_greedy<NT_SEQ>(p, b, sm.fin);
+}
+
+// ------------------------------------------------------------------------
+// Row-split kernels: statistics per (row, slice), then one finishing
+// workgroup per sequence.
+
+template <int DT, bool VEC, bool STOCH>
+__global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
+    __shared__ Scratch<NT_ROW> sc;
+    constexpr int NW = NT_ROW / 64;
+    const int per_seq = p.rows_per_seq * p.S;
+    const int b = blockIdx.x / per_seq;
+    const int item = blockIdx.x - b * per_seq;
+    const int r = item / p.S;
+    const int s = item - r * p.S;
+    const int v0 = s * p.slice_len;
+    const int v1 = min(p.V, v0 + p.slice_len);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const char* rp = STOCH ? stoch_row<DT>(p, b, r) : greedy_row<DT>(p, b, r);
+    const Row<DT, VEC> row(rp + (size_t)v0 * elem_bytes<DT>(), v1 - v0);
+    float* dst = p.part + ((size_t)b * per_seq + item) * 2;
+    if (STOCH) {
+        SoftAcc acc;
+        stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
+        float R, Z;
+        wave_softmax(acc, R, Z);
+        if (lane == 0) {
+            sc.f[wave] = R;
+            sc.g[wave] = Z;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float RR = sc.f[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) RR = fmaxf(RR, sc.f[w]);
+            float ZZ = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) ZZ += sc.g[w] * fast_exp2(sc.f[w] - RR);
+            dst[0] = RR;
+            dst[1] = ZZ;
+        }
+    } else {
+        ArgAcc acc;
+        stream_argmax<DT, VEC, NT_ROW>(row, acc);
+        wave_argmax(acc.best, acc.pos);
+        if (lane == 0) {
+            sc.f[wave] = acc.best;
+            sc.i[wave] = acc.pos;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float best = sc.f[0];
+            int pos = sc.i[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w)
+                if (argmax_better(sc.f[w], sc.i[w], best, pos)) {
+                    best = sc.f[w];
+                    pos = sc.i[w];
+                }
+            dst[0] = best;
+            dst[1] = __int_as_float(v0 + argmax_refine(row, best, pos));
+        }
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_FIN) void k_stochastic_finish(Params p) {
+    __shared__ StochFin<NT_FIN> sm;
+    const int b = blockIdx.x;
+    const int S = p.S;
+    const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
+    for (int r = threadIdx.x; r < p.rows_per_seq; r += NT_FIN) {
+        float R = -FLT_MAX;
+        for (int j = 0; j < S; ++j) R = fmaxf(R, part[(r * S + j) * 2]);
+        float Z = 0.0f;
+        for (int j = 0; j < S; ++j)
+            Z += part[(r * S + j) * 2 + 1] * fast_exp2(part[(r * S + j) * 2] - R);
+        sm.R[r] = R;
+        sm.Z[r] = Z;
+    }
+    __syncthreads();
+    finish_stochastic<DT, VEC, NT_FIN>(p, b, sm);
+}
+
+__global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
+    __shared__ GreedyFin<NT_FIN> sm;
+    const int b = blockIdx.x;
+    const int S = p.S;
+    const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
+    for (int r = threadIdx.x; r < p.rows_per_seq; r += NT_FIN) {
+        float best = part[(r * S) * 2];
+        int idx = __float_as_int(part[(r * S) * 2 + 1]);
+        for (int j = 1; j < S; ++j) {
+            const float m = part[(r * S + j) * 2];
+            if (m > best) {  // earlier slices hold lower indices: they win ties
+                best = m;
+                idx = __float_as_int(part[(r * S + j) * 2 + 1]);
+            }
+        }
+        sm.g[r] = idx;
+    }
+    __syncthreads();
+    finish_greedy<NT_FIN>(p, b, sm);
+}
+
+// ------------------------------------------------------------------------
 template <typename K>
-static int launch(K kernel, const Params& p, void* stream) {
-    const long long grid = (long long)p.B * p.rows_per_seq * p.S;
+static int launch1(K kernel, const Params& p, long long grid, int block, void* stream) {
     Params pc = p;
     void* args[] = {&pc};
     return (int)hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid),
-                                dim3(NT), args, 0, static_cast<hipStream_t>(stream));
+                                dim3(block), args, 0, static_cast<hipStream_t>(stream));
 }
 
-int launch_stochastic(const Params& p, int dtype, bool vec, void* stream) {
-    if (dtype == 1)
-        return vec ? launch(k_verify_stochastic<1, true>, p, stream)
-                   : launch(k_verify_stochastic<1, false>, p, stream);
-    return vec ? launch(k_verify_stochastic<0, true>, p, stream)
-               : launch(k_verify_stochastic<0, false>, p, stream);
+template <int DT, bool VEC>
+static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
+    if (seq) return launch1(k_stochastic_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+    const long long items = (long long)p.B * p.rows_per_seq * p.S;
+    int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
+    if (e) return e;
+    return launch1(k_stochastic_finish<DT, VEC>, p, p.B, NT_FIN, stream);
 }
 
-int launch_greedy(const Params& p, int dtype, bool vec, void* stream) {
+template <int DT, bool VEC>
+static int launch_greedy_t(const Params& p, bool seq, void* stream) {
+    if (seq) return launch1(k_greedy_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+    const long long items = (long long)p.B * p.rows_per_seq * p.S;
+    int e = launch1(k_row_stats<DT, VEC, false>, p, items, NT_ROW, stream);
+    if (e) return e;
+    return launch1(k_greedy_finish, p, p.B, NT_FIN, stream);
+}
+
+int launch_stochastic(const Params& p, int dtype, bool vec, bool seq, void* stream) {
     if (dtype == 1)
-        return vec ? launch(k_verify_greedy<1, true>, p, stream)
-                   : launch(k_verify_greedy<1, false>, p, stream);
-    return vec ? launch(k_verify_greedy<0, true>, p, stream)
-               : launch(k_verify_greedy<0, false>, p, stream);
+        return vec ? launch_stochastic_t<1, true>(p, seq, stream)
+                   : launch_stochastic_t<1, false>(p, seq, stream);
+    return vec ? launch_stochastic_t<0, true>(p, seq, stream)
+               : launch_stochastic_t<0, false>(p, seq, stream);
+}
+
+int launch_greedy(const Params& p, int dtype, bool vec, bool seq, void* stream) {
+    if (dtype == 1)
+        return vec ? launch_greedy_t<1, true>(p, seq, stream) : launch_greedy_t<1, false>(p, seq, stream);
+    return vec ? launch_greedy_t<0, true>(p, seq, stream) : launch_greedy_t<0, false>(p, seq, stream);
 }
 
 }  // namespace sv

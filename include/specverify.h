@@ -59,11 +59,13 @@
  * page, section "Inferencia so špekulatívnym dekódovaním": the accepted
  * length decides the next step's shape).
  *
- * Workspace.  sv_workspace_bytes() gives the size for a shape; pass at least
- * that many bytes, 256-byte aligned, ZERO-FILLED before its first use.  Every
- * call returns it to all zeros by the time it completes, so one workspace
- * serves any sequence of calls on one stream.  Two calls that overlap in time
- * on the same workspace race.
+ * Workspace.  sv_workspace_bytes() gives the scratch size for a shape: 0 when
+ * the batch fills the GPU on its own (one candidate and B >= 192: every
+ * sequence is then verified by a single workgroup that needs no scratch),
+ * otherwise room for 8 bytes of statistics per row slice.  Pass at least that
+ * many bytes, 256-byte aligned (NULL is accepted when the size is 0).  Its
+ * contents on entry do not matter and are unspecified on return.  Two calls
+ * that overlap in time on the same workspace race.
  *
  * Errors.  Arguments are checked on the host before anything is launched; on
  * an error nothing is written and a negative SV_ERR_* status is returned.

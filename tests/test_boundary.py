@@ -68,16 +68,21 @@ def test_status_strings(lib):
 def test_workspace_bytes(lib):
     f = lib.sv_workspace_bytes
     assert f(0, 1, 1, 1) == 0 or f(0, 1, 1, 1) % 256 == 0
-    for args in [(256, 1, 8, 128256), (64, 1, 4, 128256), (1, 1, 4, 32000), (32, 16, 4, 32000),
-                 (512, 1, 3, 129280)]:
+    for args in [(64, 1, 4, 128256), (1, 1, 4, 32000), (32, 16, 4, 32000), (191, 1, 8, 1000),
+                 (256, 2, 8, 1000)]:
         n = f(*args)
         assert n > 0 and n % 8 == 0
+    # one candidate and B >= 192: one workgroup per sequence, no scratch
+    for args in [(192, 1, 8, 128256), (256, 1, 8, 128256), (512, 1, 3, 129280)]:
+        assert f(*args) == 0
     # bad shapes
     for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, 0, 10), (1, 1, 1, 0), (1, 1, 65, 10),
                  (1, 600, 1, 10)]:
         assert f(*args) == 0
-    # larger batches never need less
-    assert f(512, 1, 8, 128256) >= f(256, 1, 8, 128256)
+    # row-split: at least 8 bytes per row of every sequence
+    for B in (1, 50, 100, 150, 191):
+        assert f(B, 1, 8, 128256) >= B * 17 * 8
+    assert f(32, 16, 4, 32000) >= 32 * 16 * 5 * 8
 
 
 # Fake, well-aligned device addresses: the checks below fail before any
@@ -128,8 +133,11 @@ def test_greedy_shape(lib, kw):
 
 
 def test_grid_too_large(lib):
-    # 2^24 workgroups would overflow the 32-bit launch size
-    assert greedy(lib, B=1 << 21, G=1, k=7, V=10, rs=10) == SV_ERR_SHAPE
+    # the launch's thread count must fit in 32 bits: 2^25 row-split groups of
+    # 256 threads, or 2^22 sequence-resident groups of 1024, are too many
+    assert greedy(lib, B=1 << 21, G=2, k=7, V=10, rs=10) == SV_ERR_SHAPE
+    assert greedy(lib, B=1 << 22, G=1, k=7, V=10, rs=10) == SV_ERR_SHAPE
+    assert stoch(lib, B=1 << 22, k=7, V=10, rs=10) == SV_ERR_SHAPE
 
 
 def test_dtype(lib):
@@ -147,6 +155,14 @@ def test_workspace_checks(lib):
     assert stoch(lib, wsb=need - 1) == SV_ERR_WORKSPACE
     assert stoch(lib, ws=ctypes.c_void_p((1 << 21) + 16)) == SV_ERR_WORKSPACE
     assert greedy(lib, wsb=8) == SV_ERR_WORKSPACE
+
+
+def test_workspace_optional_without_scratch(lib):
+    # B >= 192, one candidate: no workspace needed, so NULL passes the checks
+    # (the call then fails at the launch on a machine without a GPU, or runs)
+    assert lib.sv_workspace_bytes(200, 1, 3, 100) == 0
+    # B < 192 still needs it
+    assert stoch(lib, B=100, ws=None) == SV_ERR_NULL
 
 
 def test_empty_batch_is_a_noop(lib):
