@@ -42,6 +42,14 @@ def algorithmic_bytes(spec, mode: str) -> int:
     return B * G * (k + 1) * V * s + 4 * B * G * k + 4 * B + 4 * B * (k + 1) + 4 * B
 
 
+def kernel_name(spec, mode: str) -> str:
+    """The kernel that dominates a call: one workgroup per sequence for large
+    single-candidate batches, else the row-statistics kernel."""
+    if spec.G == 1 and spec.B >= 192:
+        return f"k_{mode}_seq"
+    return "k_row_stats"
+
+
 def kernel_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -192,7 +200,7 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for(spec.index, mode),
                      "algorithmic_bytes": nbytes,
-                     "kernel": f"k_verify_{mode}"},
+                     "kernel": kernel_name(spec, mode)},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
