@@ -165,7 +165,16 @@ def main():
     best = torch.empty(spec.B, dtype=torch.int32, device=dev)
 
     if mode == "stochastic":
+        # With the p/q diagnostics requested every position of every sequence
+        # is evaluated: the full read of all B(2k+1) rows that the headline
+        # figure is quoted on, independent of where the first rejection falls.
+        dbg = torch.empty((spec.B, spec.k, 2), dtype=torch.float32, device=dev)
+
         def step():
+            binding.sv_verify_stochastic(t, d, x, ua, us, spec.tau, accept_len=accept,
+                                         tokens=tokens, dbg_px_qx=dbg)
+
+        def step_early_exit():
             binding.sv_verify_stochastic(t, d, x, ua, us, spec.tau, accept_len=accept,
                                          tokens=tokens)
     else:
@@ -203,6 +212,23 @@ def main():
                      "kernel": kernel_name(spec, mode)},
         "wall_s_timed": round(wall, 3),
     }
+    if mode == "stochastic" and spec.G == 1 and spec.B >= 192:
+        # Separate line: without diagnostics a sequence stops reading at its
+        # first rejection.  Bytes are the rows that must then be read (the
+        # pairs up to the first rejection, or all rows if none), from the
+        # accepted lengths of this batch; the rocprof-counted fetch is in
+        # profiles/ when taken.
+        ms_x, _ = time_calls(step_early_exit, args.steps, args.warmup, torch)
+        a_host = accept.cpu().numpy()
+        s_b = 2 if spec.dtype == 1 else 4
+        rows = sum(2 * int(a) + 2 if a < spec.k else 2 * spec.k + 1 for a in a_host)
+        nb_x = rows * spec.V * s_b + nbytes - spec.B * (2 * spec.k + 1) * spec.V * s_b
+        result["early_exit"] = {
+            "value": round(spec.B / (ms_x * 1e-3), 1), "unit": "seqs/s",
+            "ms_per_step": round(ms_x, 5), "rows_read": rows,
+            "bytes_needed": nb_x, "GBps_on_bytes_needed": round(nb_x / (ms_x * 1e-3) / 1e9, 1),
+            "mean_accept_len": round(float(a_host.mean()), 4),
+            "traffic": traffic_for(spec.index, "stochastic_early_exit")}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(batch, mode)

@@ -118,6 +118,7 @@ struct Row<DT, true> {
     __amdgpu_buffer_rsrc_t rs;
     const char* base;
     int n, nch;
+    Row() = default;
     __device__ __forceinline__ Row(const char* p, int n_) : base(p), n(n_), nch(n_ / E) {
         rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, nch * 16,
                                                RSRC_WORD3);
@@ -141,6 +142,7 @@ struct Row<DT, false> {
     static constexpr int E = 1;
     const char* base;
     int n, nch;
+    Row() = default;
     __device__ __forceinline__ Row(const char* p, int n_) : base(p), n(n_), nch(n_) {}
     __device__ __forceinline__ C chunk_at(int i, int s) const {
         C c;
@@ -400,36 +402,51 @@ __device__ __forceinline__ int argmax_refine(const Row<DT, VEC>& row, float best
 // Inverse-CDF draw over one row (or a row pair) with weights W(t[, d]):
 // the first index whose cumulative weight exceeds r * total; if rounding
 // leaves none, the last index with positive weight (0 if there is none).
-// The row is cut into tiles of NT*m chunks; pass A sums each tile, a block
-// scan over tile sums finds the tile holding the draw, pass B scans inside
-// that tile.  *total gets the total weight.  All threads call.
+//
+// The row's whole chunks are cut into tiles of NT*m chunks (m block-wide
+// rounds of NT chunks, at most MAX_TILES tiles); the n % E trailing logits
+// form one more tile.  Pass A sums every tile into LDS, one slot per wave
+// (tile_part[tile * NW + wave]); a block scan over tile sums then finds the
+// tile holding r * total and pass B scans inside that tile.
+
+struct TileGeom {
+    int nch, rem, rounds, m, ntiles, nt_all;
+};
+
+template <int NT>
+__device__ __forceinline__ TileGeom tile_geom(int nch, int rem) {
+    TileGeom g;
+    g.nch = nch;
+    g.rem = rem;
+    g.rounds = (nch + NT - 1) / NT;
+    g.m = max(1, (g.rounds + MAX_TILES - 1) / MAX_TILES);
+    g.ntiles = (g.rounds + g.m - 1) / g.m;
+    g.nt_all = g.ntiles + (rem > 0 ? 1 : 0);
+    return g;
+}
+
+template <bool PAIR, typename C, typename Wt>
+__device__ __forceinline__ float chunk_weight_sum(const Wt& wf, const C& t, const C& d) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C::E; ++e) acc += PAIR ? wf(t.get(e), d.get(e)) : wf(t.get(e), 0.0f);
+    return acc;
+}
+
+// Pass A over whole block-wide rounds (no barriers; tile_part pre-zeroed).
 template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
-__device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const Wt& wf, float r,
-                               float* total_out, float* tile_part, float* tile_excl,
-                               Scratch<NT>& sc) {
+__device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
+                                                 const Wt& wf, const TileGeom& g,
+                                                 float* tile_part) {
     using C = Chunk<DT, VEC>;
-    constexpr int E = C::E;
     constexpr int NW = NT / 64;
-    const Row<DT, VEC> tr(trow, V);
-    const Row<DT, VEC> dr(PAIR ? drow : trow, V);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nch = tr.nch;
-    const int rem = VEC ? V - nch * E : 0;
-    const int rounds = (nch + NT - 1) / NT;                      // block-wide rounds of chunks
-    const int m = max(1, (rounds + MAX_TILES - 1) / MAX_TILES);  // rounds per tile
-    const int ntiles = (rounds + m - 1) / m;
-    const int nt_all = ntiles + (rem > 0 ? 1 : 0);               // trailing logits = last tile
-
-    for (int t = tid; t < nt_all * NW; t += NT) tile_part[t] = 0.0f;
-    __syncthreads();
-
-    // Pass A: per-tile partial sums, one slot per wave.
-    for (int r0 = 0; r0 < rounds; r0 += TUNROLL) {
+    for (int r0 = 0; r0 < g.rounds; r0 += TUNROLL) {
         C tb[TUNROLL], db[TUNROLL];
 #pragma unroll
         for (int u = 0; u < TUNROLL; ++u) {
             const int ci = (r0 + u) * NT + tid;
-            if (ci < nch) {
+            if (ci < g.nch) {
                 tb[u] = tr.chunk(ci);
                 if (PAIR) db[u] = dr.chunk(ci);
             } else {
@@ -440,36 +457,51 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
 #pragma unroll
         for (int u = 0; u < TUNROLL; ++u) {
             const int round = r0 + u;
-            if (round < rounds) {  // uniform across the block
-                float acc = 0.0f;
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    acc += PAIR ? wf(tb[u].get(e), db[u].get(e)) : wf(tb[u].get(e), 0.0f);
-                acc = wave_sum(acc);
-                if (lane == 0) tile_part[(round / m) * NW + wave] += acc;
+            if (round < g.rounds) {  // uniform across the block
+                const float acc = wave_sum(chunk_weight_sum<PAIR>(wf, tb[u], db[u]));
+                if (lane == 0) tile_part[(round / g.m) * NW + wave] += acc;
             }
         }
     }
-    if (rem > 0) {
-        float w = 0.0f;
-        if (tid < rem) {
-            const float tv = tr.elem(nch * E + tid);
-            const float dv = PAIR ? dr.elem(nch * E + tid) : 0.0f;
-            w = wf(tv, dv);
-        }
-        w = wave_sum(w);
-        if (lane == 0) tile_part[ntiles * NW + wave] += w;
-    }
-    __syncthreads();
+}
 
+// The trailing-logits tile (no barriers; tile_part pre-zeroed).
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+__device__ __forceinline__ void cdf_trailing(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
+                                             const Wt& wf, const TileGeom& g, float* tile_part) {
+    constexpr int NW = NT / 64;
+    constexpr int E = Chunk<DT, VEC>::E;
+    if (g.rem == 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float w = 0.0f;
+    if (tid < g.rem) {
+        const float tv = tr.elem(g.nch * E + tid);
+        const float dv = PAIR ? dr.elem(g.nch * E + tid) : 0.0f;
+        w = wf(tv, dv);
+    }
+    w = wave_sum(w);
+    if (lane == 0) tile_part[g.ntiles * NW + wave] += w;
+}
+
+// Scan over tile sums, then pass B.  tile_part must be complete (after a
+// barrier).  *total_out gets the total weight.  All threads call.
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+__device__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const Wt& wf, float r,
+                          const TileGeom& g, float* total_out, const float* tile_part,
+                          float* tile_excl, Scratch<NT>& sc) {
+    using C = Chunk<DT, VEC>;
+    constexpr int E = C::E;
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x;
+    const int nch = g.nch, rem = g.rem;
     // Block scan over tiles (each thread owns a contiguous run of tiles).
-    const int tpt = (nt_all + NT - 1) / NT;  // tiles per thread, <= 2
+    const int tpt = (g.nt_all + NT - 1) / NT;  // tiles per thread, <= 2
     float mine[2] = {0.0f, 0.0f};
     float run = 0.0f;
     for (int j = 0; j < tpt; ++j) {
         const int t = tid * tpt + j;
         float s = 0.0f;
-        if (t < nt_all) {
+        if (t < g.nt_all) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) s += tile_part[t * NW + w];
         }
@@ -484,7 +516,7 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
         float acc = excl;
         for (int j = 0; j < tpt; ++j) {
             const int t = tid * tpt + j;
-            if (t < nt_all) {
+            if (t < g.nt_all) {
                 tile_excl[t] = acc;
                 if (cross == INT_MAX && acc + mine[j] > T) cross = t;
                 acc += mine[j];
@@ -518,7 +550,7 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
     float cum = tile_excl[cross];
     int found = INT_MAX;
     int tile_last = -1;
-    if (cross == ntiles) {  // the trailing-logits tile
+    if (cross == g.ntiles) {  // the trailing-logits tile
         float w = 0.0f;
         if (tid < rem) {
             const float tv = tr.elem(nch * E + tid);
@@ -531,7 +563,7 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
         if (w > 0.0f && cum + (ex + w) > T) found = nch * E + tid;
         found = block_min_i<NT>(found, sc);
     } else {
-        for (int rd = cross * m; rd < min(rounds, (cross + 1) * m); ++rd) {
+        for (int rd = cross * g.m; rd < min(g.rounds, (cross + 1) * g.m); ++rd) {
             const int ci = rd * NT + tid;
             float wv[E];
             float loc = 0.0f;
@@ -565,6 +597,24 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
     }
     if (found != INT_MAX) return found;
     return max(block_max_i<NT>(tile_last, sc), 0);
+}
+
+// The whole draw in one call.  All threads call.
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+__device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const Wt& wf, float r,
+                               float* total_out, float* tile_part, float* tile_excl,
+                               Scratch<NT>& sc) {
+    constexpr int NW = NT / 64;
+    const Row<DT, VEC> tr(trow, V);
+    const Row<DT, VEC> dr(PAIR ? drow : trow, V);
+    const int tid = threadIdx.x;
+    const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * Chunk<DT, VEC>::E : 0);
+    for (int t = tid; t < g.nt_all * NW; t += NT) tile_part[t] = 0.0f;
+    __syncthreads();
+    cdf_pass_a_block<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part);
+    cdf_trailing<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part);
+    __syncthreads();
+    return cdf_select<DT, VEC, PAIR, NT>(tr, dr, wf, r, g, total_out, tile_part, tile_excl, sc);
 }
 
 // Residual weight max(0, p - q) of one row pair, with each normaliser
@@ -727,6 +777,18 @@ __device__ void finish_greedy(const Params& p, int b, GreedyFin<NT>& sm) {
 // ------------------------------------------------------------------------
 // Sequence-resident kernels: one workgroup per sequence.
 
+// Merge the per-wave partial normalisers of row r: R = max, Z rescaled sum.
+template <int NW>
+__device__ __forceinline__ void merge_row(const float* wR, const float* wZ, int r, float& R,
+                                          float& Z) {
+    R = wR[r * NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) R = fmaxf(R, wR[r * NW + w]);
+    Z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Z += wZ[r * NW + w] * fast_exp2(wR[r * NW + w] - R);
+}
+
 struct StochSeqSmem {
     StochFin<NT_SEQ> fin;
     float wR[MAX_ROWS_STOCH * (NT_SEQ / 64)];  // per-wave partial normalisers
@@ -770,6 +832,128 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
     }
     __syncthreads();
     finish_stochastic<DT, VEC, NT_SEQ>(p, b, sm.fin);
+}
+
+// Early-exit variant, used when no per-position diagnostics are asked for:
+// rows stream in position order and a sequence stops reading at its first
+// rejection, because no later row can change accept_len or tokens.  One
+// block-wide decision per position: after pair i every thread merges the
+// pair's per-wave partials from LDS and reaches the same verdict.
+struct StochExitSmem {
+    StochFin<NT_SEQ> fin;
+    float wR[2 * 2 * (NT_SEQ / 64)];  // [pair parity][target, draft][wave]
+    float wZ[2 * 2 * (NT_SEQ / 64)];
+    int xv[kMaxK];    // draft tokens
+    float uv[kMaxK];  // acceptance uniforms
+    float tv[kMaxK];  // target logit at the draft token (0 if out of range)
+    float dv[kMaxK];  // draft logit at the draft token
+};
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
+    constexpr int NT = NT_SEQ;
+    constexpr int NW = NT / 64;
+    __shared__ StochExitSmem sm;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int k = p.k, V = p.V;
+    const float c = p.c;
+    const int32_t* x = p.tokens_in + (size_t)b * k;
+    // Wave 0 gathers the tokens, uniforms and the logits at the tokens (lane
+    // i: position i) while it streams the first row; the first barrier
+    // publishes them.
+    const bool gather = wave == 0 && lane < k;
+    int gx = -1;
+    float gu = 0.0f, gt = 0.0f, gd = 0.0f;
+    if (gather) {
+        gx = x[lane];
+        gu = p.u_accept[(size_t)b * k + lane];
+    }
+    int a = k;
+    float Rt = 0.0f, Zt = 1.0f, Rd = 0.0f, Zd = 1.0f;
+    for (int i = 0; i < k; ++i) {
+        float* wR = sm.wR + (i & 1) * 2 * NW;
+        float* wZ = sm.wZ + (i & 1) * 2 * NW;
+        for (int half = 0; half < 2; ++half) {
+            const Row<DT, VEC> row(stoch_row<DT>(p, b, half == 0 ? i : k + 1 + i), V);
+            SoftAcc acc;
+            stream_softmax<DT, VEC, NT>(row, c, acc);
+            float R, Z;
+            wave_softmax(acc, R, Z);
+            if (lane == 0) {
+                wR[half * NW + wave] = R;
+                wZ[half * NW + wave] = Z;
+            }
+            if (i == 0 && half == 0 && gather && gx >= 0 && gx < V) {
+                gt = load_elem<DT>(stoch_row<DT>(p, b, lane), gx);
+                gd = load_elem<DT>(stoch_row<DT>(p, b, k + 1 + lane), gx);
+            }
+        }
+        if (i == 0 && gather) {
+            sm.xv[lane] = gx;
+            sm.uv[lane] = gu;
+            sm.tv[lane] = gt;
+            sm.dv[lane] = gd;
+        }
+        // One barrier per pair; the partials are double-buffered by pair
+        // parity, so the next pair never overwrites what is being read.
+        __syncthreads();
+        merge_row<NW>(wR, wZ, 0, Rt, Zt);
+        merge_row<NW>(wR, wZ, 1, Rd, Zd);
+        const int xi = sm.xv[i];
+        float pi = 0.0f, qi = 0.0f;
+        if (xi >= 0 && xi < V) {
+            pi = fast_exp2(fmaf(sm.tv[i], c, -Rt)) / Zt;
+            qi = fast_exp2(fmaf(sm.dv[i], c, -Rd)) / Zd;
+        }
+        if (!(sm.uv[i] * qi < pi)) {  // the same verdict in every thread
+            a = i;
+            break;
+        }
+    }
+    int32_t* out = p.tokens_out + (size_t)b * (k + 1);
+    for (int i = tid; i <= k; i += NT) {
+        if (i < a) out[i] = x[i];
+        else if (i > a) out[i] = -1;
+    }
+    const float rr = p.u_sample[b];
+    float total = 0.0f;
+    int y;
+    if (a < k) {
+        const ResidualW w{c, -(Rt + __log2f(Zt)), -(Rd + __log2f(Zd))};
+        y = inverse_cdf_row<DT, VEC, true, NT>(stoch_row<DT>(p, b, a), stoch_row<DT>(p, b, k + 1 + a),
+                                               V, w, rr, &total, sm.fin.tile_part,
+                                               sm.fin.tile_excl, sm.fin.sc);
+        if (!(total > 0.0f)) {
+            // p == q to float precision: the residual is empty; draw from p_a.
+            const TargetW tw{c, -Rt};
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, a), nullptr, V, tw, rr,
+                                                    &total, sm.fin.tile_part, sm.fin.tile_excl,
+                                                    sm.fin.sc);
+        }
+    } else {
+        // every draft token accepted: the bonus token from row k
+        const Row<DT, VEC> row(stoch_row<DT>(p, b, k), V);
+        SoftAcc acc;
+        stream_softmax<DT, VEC, NT>(row, c, acc);
+        float R, Z;
+        wave_softmax(acc, R, Z);
+        if (lane == 0) {
+            sm.wR[(k & 1) * 2 * NW + wave] = R;
+            sm.wZ[(k & 1) * 2 * NW + wave] = Z;
+        }
+        __syncthreads();
+        float Rk, Zk;
+        merge_row<NW>(sm.wR + (k & 1) * 2 * NW, sm.wZ + (k & 1) * 2 * NW, 0, Rk, Zk);
+        (void)Zk;
+        const TargetW tw{c, -Rk};
+        y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, k), nullptr, V, tw, rr, &total,
+                                                sm.fin.tile_part, sm.fin.tile_excl, sm.fin.sc);
+    }
+    if (tid == 0) {
+        out[a] = y;
+        p.accept_len[b] = a;
+    }
 }
 
 struct GreedySeqSmem {
@@ -925,7 +1109,9 @@ static int launch1(K kernel, const Params& p, long long grid, int block, void* s
 
 template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
-    if (seq) return launch1(k_stochastic_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+    if (seq)
+        return p.dbg ? launch1(k_stochastic_seq<DT, VEC>, p, p.B, NT_SEQ, stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC>, p, p.B, NT_SEQ, stream);
     const long long items = (long long)p.B * p.rows_per_seq * p.S;
     int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
     if (e) return e;

@@ -118,6 +118,13 @@ extern "C" {
  *   dbg_px_qx      optional out float [B][k][2]: p_i(x_i), q_i(x_i) for every
  *                  position (NULL to skip)
  * B == 0 is a no-op that returns SV_OK.
+ *
+ * Rows after a sequence's first rejection cannot change accept_len or
+ * tokens.  Without dbg_px_qx, a batch large enough to give every sequence its
+ * own workgroup (B >= 192) stops reading a sequence at its first rejection
+ * (the "early termination" of Novita's verification strategy, read as
+ * stopping at the first mismatch); with dbg_px_qx every position of every
+ * sequence is evaluated.  The outputs are the same either way.
  */
 int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept,

@@ -53,16 +53,27 @@ def dev(a):
 
 
 def run_stochastic(t, d, x, ua, us, tau, dtype, pad=0, unaligned=False):
+    """Both ways of calling: with p/q diagnostics (every position evaluated)
+    and without (a sequence may stop reading at its first rejection).  Each
+    is compared with the oracle; the reports are merged."""
     B, k1, V = t.shape
     k = k1 - 1
     tt, th, rs = logits_to_device(t, dtype, pad, unaligned)
     dt, dh, _ = logits_to_device(d, dtype, pad, unaligned)
+    xd, uad, usd = dev(x), dev(ua), dev(us)
     dbg = torch.full((B, k, 2), -1.0, dtype=torch.float32, device=DEV)
-    a, tok = binding.sv_verify_stochastic(tt, dt, dev(x), dev(ua), dev(us), tau, dbg_px_qx=dbg)
+    a, tok = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau, dbg_px_qx=dbg)
+    a2, tok2 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau)
     torch.cuda.synchronize()
     rep = protocol.compare_stochastic(th, dh, x, ua, us, B=B, k=k, V=V, temperature=tau,
                                       accept_len=a.cpu().numpy(), tokens=tok.cpu().numpy(),
                                       px_qx=dbg.cpu().numpy(), row_stride=rs)
+    rep2 = protocol.compare_stochastic(th, dh, x, ua, us, B=B, k=k, V=V, temperature=tau,
+                                       accept_len=a2.cpu().numpy(), tokens=tok2.cpu().numpy(),
+                                       row_stride=rs)
+    rep.failures += ["(no diagnostics) " + f for f in rep2.failures]
+    rep.decision_band += rep2.decision_band
+    rep.token_band += rep2.token_band
     return rep, a.cpu().numpy(), tok.cpu().numpy()
 
 
@@ -288,9 +299,10 @@ def test_deterministic(index):
     for _ in range(5):
         dbg = torch.empty((s.B, s.k, 2), dtype=torch.float32, device=DEV)
         a, tok = binding.sv_verify_stochastic(tt, dt, x, ua, us, s.tau, dbg_px_qx=dbg)
+        a3, tok3 = binding.sv_verify_stochastic(tt, dt, x, ua, us, s.tau)
         a2, tok2, _ = binding.sv_verify_greedy(tt, x)
         torch.cuda.synchronize()
-        outs.append([o.cpu().numpy() for o in (a, tok, dbg, a2, tok2)])
+        outs.append([o.cpu().numpy() for o in (a, tok, dbg, a3, tok3, a2, tok2)])
     for o in outs[1:]:
         for u, v in zip(outs[0], o):
             assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
