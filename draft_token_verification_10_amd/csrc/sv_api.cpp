@@ -35,12 +35,13 @@ struct Plan {
     int rows_per_seq;
     int S;
     int slice_len;
+    int SD;  // row-split stochastic: draw workgroups per sequence
     bool vec;
     size_t ws_bytes;
 };
 
 int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dtype,
-              const void* const* row_bases, int n_bases, Plan* pl) {
+              bool stochastic, const void* const* row_bases, int n_bases, Plan* pl) {
     const int es = elem_size(dtype);
     bool vec = ((row_stride * es) % 16) == 0;
     for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
@@ -49,6 +50,7 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     pl->vec = vec;
     if (pl->seq) {
         pl->S = 1;
+        pl->SD = 1;
         pl->slice_len = V;
         pl->ws_bytes = 0;
         return B > kMaxSeqGrid ? SV_ERR_SHAPE : SV_OK;
@@ -63,7 +65,9 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
     pl->S = S;
     pl->slice_len = slice_len;
-    pl->ws_bytes = sv::workspace_bytes_for(B, rows_per_seq, S);
+    pl->SD = stochastic ? sv::plan_draw_slices(B, sv::draw_tiles(V / E, V % E)) : 1;
+    if ((long long)B * pl->SD > kMaxGrid) return SV_ERR_SHAPE;
+    pl->ws_bytes = sv::workspace_bytes_for(B, rows_per_seq, S, stochastic);
     return SV_OK;
 }
 
@@ -77,9 +81,10 @@ int check_workspace(const void* ws, size_t bytes, const Plan& pl) {
 
 // Workspace bytes for one entry point at this shape (an upper bound over the
 // load paths: the slice count before rounding to whole chunks).
-size_t workspace_need(int B, int G, int rows_per_seq, int V) {
+size_t workspace_need(int B, int G, int rows_per_seq, int V, bool stochastic) {
     if (sv::use_seq_resident(B, G)) return 0;
-    return sv::workspace_bytes_for(B, rows_per_seq, sv::plan_slices((long long)B * rows_per_seq, V));
+    return sv::workspace_bytes_for(B, rows_per_seq, sv::plan_slices((long long)B * rows_per_seq, V),
+                                   stochastic);
 }
 
 }  // namespace
@@ -91,8 +96,8 @@ extern "C" {
 size_t sv_workspace_bytes(int B, int G, int k, int V) {
     if (check_shape(B, G, k, V, V) != SV_OK) return 0;
     // Enough for either entry point: stochastic (one candidate) and greedy.
-    const size_t s = workspace_need(B, 1, 2 * k + 1, V);
-    const size_t g = workspace_need(B, G, G * (k + 1), V);
+    const size_t s = workspace_need(B, 1, 2 * k + 1, V, true);
+    const size_t g = workspace_need(B, G, G * (k + 1), V, false);
     return s > g ? s : g;
 }
 
@@ -127,7 +132,7 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
         return SV_ERR_NULL;
     const void* bases[2] = {target_logits, draft_logits};
     Plan pl;
-    st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, bases, 2, &pl);
+    st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, true, bases, 2, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;
@@ -143,6 +148,12 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
     p.best_cand = nullptr;
     p.dbg = dbg_px_qx;
     p.part = static_cast<float*>(workspace);
+    if (!pl.seq) {
+        char* w = static_cast<char*>(workspace) + sv::part_bytes(B, pl.rows_per_seq, pl.S);
+        p.tilesum = reinterpret_cast<float*>(w);
+        p.meta = reinterpret_cast<int*>(w + sv::tilesum_bytes(B));
+    }
+    p.SD = pl.SD;
     p.row_stride = row_stride;
     p.B = B;
     p.G = 1;
@@ -166,7 +177,7 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     if (!target_logits || !draft_tokens || !accept_len || !tokens) return SV_ERR_NULL;
     const void* bases[1] = {target_logits};
     Plan pl;
-    st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, bases, 1, &pl);
+    st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, false, bases, 1, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;

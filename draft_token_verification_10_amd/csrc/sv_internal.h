@@ -43,9 +43,42 @@ inline int plan_slices(long long rows, int V) {
     return (int)s;
 }
 
-// Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S].
-inline size_t workspace_bytes_for(int B, int rows_per_seq, int S) {
-    return (size_t)B * rows_per_seq * S * 8;
+// Inverse-CDF tiles: a row's chunks are cut into at most kMaxTiles tiles of
+// whole 256-chunk rounds, plus one tile for its trailing logits.
+constexpr int kMaxTiles = 256;
+constexpr int kDrawRound = 256;  // chunks per round in the row-split draw
+
+inline int draw_tiles(int nch, int rem) {
+    const int rounds = (nch + kDrawRound - 1) / kDrawRound;
+    int m = (rounds + kMaxTiles - 1) / kMaxTiles;
+    if (m < 1) m = 1;
+    return (rounds + m - 1) / m + (rem > 0 ? 1 : 0);
+}
+
+// The row-split stochastic draw gives every sequence SD workgroups, so that
+// about kDrawTargetItems workgroups share it.
+constexpr int kDrawTargetItems = 1024;
+
+inline int plan_draw_slices(int B, int tiles) {
+    int sd = B > 0 ? (kDrawTargetItems + B - 1) / B : 1;
+    if (sd > tiles) sd = tiles;
+    if (sd < 1) sd = 1;
+    return sd;
+}
+
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S],
+// then (stochastic only) tile sums float [B][kMaxTiles + 1] and the per
+// sequence draw parameters int4 [B].
+inline size_t part_bytes(int B, int rows_per_seq, int S) {
+    return round256((size_t)B * rows_per_seq * S * 8);
+}
+inline size_t tilesum_bytes(int B) { return round256((size_t)B * (kMaxTiles + 1) * 4); }
+inline size_t workspace_bytes_for(int B, int rows_per_seq, int S, bool stochastic) {
+    size_t n = part_bytes(B, rows_per_seq, S);
+    if (stochastic) n += tilesum_bytes(B) + round256((size_t)B * 16);
+    return n;
 }
 
 struct Params {
@@ -59,6 +92,9 @@ struct Params {
     int32_t* best_cand;
     float* dbg;
     float* part;          // row-split only: [B][rows_per_seq][S][2]
+    float* tilesum;       // row-split stochastic: [B][kMaxTiles + 1]
+    int* meta;            // row-split stochastic: [B][4] draw parameters
+    int SD;               // row-split stochastic: draw workgroups per sequence
     long long row_stride; // elements
     int B, G, k, V;
     int rows_per_seq;     // stochastic 2k+1, greedy G(k+1)

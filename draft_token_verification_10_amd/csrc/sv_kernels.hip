@@ -37,7 +37,7 @@ constexpr int NT_ROW = 256;    // row-split statistics workgroup: 4 wave64s
 constexpr int NT_FIN = 1024;   // row-split finishing workgroup
 constexpr int UNROLL = 4;      // 16-byte loads in flight per lane while streaming
 constexpr int TUNROLL = 4;     // chunk pairs in flight per lane while sampling
-constexpr int MAX_TILES = 256; // inverse-CDF tiles held in LDS
+constexpr int MAX_TILES = kMaxTiles; // inverse-CDF tiles held in LDS
 constexpr int MAX_ROWS_STOCH = 2 * kMaxK + 1;
 constexpr int MAX_ROWS_GREEDY_SEQ = kMaxK + 1;
 // How far (log2 units) a new maximum may exceed the streaming reference
@@ -49,6 +49,10 @@ constexpr int RSRC_WORD3 = 0x00020000;
 // (the sampling re-read aside), and streaming them with the non-temporal
 // hint measured about 13% faster on the B=256, k=8, V=128256 bf16 workload.
 constexpr int LOAD_POLICY_NT = 2;
+// The full-read kernel streams the pairs of the lowest positions last and
+// with ordinary loads, so that the rows a rejection most often lands on are
+// still cached when the closing-token draw reads them again.
+constexpr int KEEP_PAIRS = 1;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -123,8 +127,11 @@ struct Row<DT, true> {
         rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, nch * 16,
                                                RSRC_WORD3);
     }
+    // KEEP: an ordinary (temporal) load, for rows that will be read again soon.
+    template <bool KEEP = false>
     __device__ __forceinline__ C chunk_at(int i, int s) const {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, s * 16, LOAD_POLICY_NT);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, s * 16,
+                                                             KEEP ? 0 : LOAD_POLICY_NT);
         C c;
         c.w[0] = v[0];
         c.w[1] = v[1];
@@ -144,6 +151,7 @@ struct Row<DT, false> {
     int n, nch;
     Row() = default;
     __device__ __forceinline__ Row(const char* p, int n_) : base(p), n(n_), nch(n_) {}
+    template <bool KEEP = false>
     __device__ __forceinline__ C chunk_at(int i, int s) const {
         C c;
         c.w[0] = __float_as_uint(load_elem<DT>(base, i + s));
@@ -295,7 +303,7 @@ __device__ __forceinline__ void soft_consume(const C* buf, float c, SoftAcc& a) 
         }
 }
 
-template <int DT, bool VEC, int NT>
+template <int DT, bool VEC, int NT, bool KEEP = false>
 __device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c, SoftAcc& a) {
     using C = Chunk<DT, VEC>;
     constexpr int E = C::E;
@@ -307,11 +315,11 @@ __device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c,
         C buf[UNROLL];
         if (i0 + STEP <= nch) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) buf[u] = row.chunk_at(i, u * NT);
+            for (int u = 0; u < UNROLL; ++u) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
         } else {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                if (i + u * NT < nch) buf[u] = row.chunk_at(i, u * NT);
+                if (i + u * NT < nch) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
                 else buf[u].set_neg_inf();
             }
         }
@@ -433,15 +441,16 @@ __device__ __forceinline__ float chunk_weight_sum(const Wt& wf, const C& t, cons
     return acc;
 }
 
-// Pass A over whole block-wide rounds (no barriers; tile_part pre-zeroed).
+// Pass A over the block-wide rounds [r_begin, r_end) (no barriers;
+// tile_part pre-zeroed; tile t is stored at slot (t - tile_base) * NW).
 template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
-__device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
-                                                 const Wt& wf, const TileGeom& g,
-                                                 float* tile_part) {
+__device__ __forceinline__ void cdf_pass_a_rounds(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
+                                                  const Wt& wf, const TileGeom& g, int r_begin,
+                                                  int r_end, int tile_base, float* tile_part) {
     using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int r0 = 0; r0 < g.rounds; r0 += TUNROLL) {
+    for (int r0 = r_begin; r0 < r_end; r0 += TUNROLL) {
         C tb[TUNROLL], db[TUNROLL];
 #pragma unroll
         for (int u = 0; u < TUNROLL; ++u) {
@@ -457,18 +466,26 @@ __device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const R
 #pragma unroll
         for (int u = 0; u < TUNROLL; ++u) {
             const int round = r0 + u;
-            if (round < g.rounds) {  // uniform across the block
+            if (round < r_end) {  // uniform across the block
                 const float acc = wave_sum(chunk_weight_sum<PAIR>(wf, tb[u], db[u]));
-                if (lane == 0) tile_part[(round / g.m) * NW + wave] += acc;
+                if (lane == 0) tile_part[(round / g.m - tile_base) * NW + wave] += acc;
             }
         }
     }
 }
 
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+__device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
+                                                 const Wt& wf, const TileGeom& g,
+                                                 float* tile_part) {
+    cdf_pass_a_rounds<DT, VEC, PAIR, NT>(tr, dr, wf, g, 0, g.rounds, 0, tile_part);
+}
+
 // The trailing-logits tile (no barriers; tile_part pre-zeroed).
 template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
 __device__ __forceinline__ void cdf_trailing(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
-                                             const Wt& wf, const TileGeom& g, float* tile_part) {
+                                             const Wt& wf, const TileGeom& g, float* tile_part,
+                                             int tile_base = 0) {
     constexpr int NW = NT / 64;
     constexpr int E = Chunk<DT, VEC>::E;
     if (g.rem == 0) return;
@@ -480,7 +497,7 @@ __device__ __forceinline__ void cdf_trailing(const Row<DT, VEC>& tr, const Row<D
         w = wf(tv, dv);
     }
     w = wave_sum(w);
-    if (lane == 0) tile_part[g.ntiles * NW + wave] += w;
+    if (lane == 0) tile_part[(g.ntiles - tile_base) * NW + wave] += w;
 }
 
 // Scan over tile sums, then pass B.  tile_part must be complete (after a
@@ -811,7 +828,8 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
         const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
         const Row<DT, VEC> row(stoch_row<DT>(p, b, r), p.V);
         SoftAcc acc;
-        stream_softmax<DT, VEC, NT_SEQ>(row, p.c, acc);
+        if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT_SEQ, true>(row, p.c, acc);
+        else stream_softmax<DT, VEC, NT_SEQ>(row, p.c, acc);
         float R, Z;
         wave_softmax(acc, R, Z);
         if (lane == 0) {
@@ -1058,13 +1076,30 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
     }
 }
 
+// Row-split stochastic finish, in two kernels so that the closing-token draw
+// -- one or two full rows per sequence -- is spread over SD workgroups per
+// sequence instead of one:
+//   k_draw_tiles  (B*SD groups): every group merges its sequence's
+//     statistics and takes the decisions itself (cheap, and it saves a
+//     launch), then sums the draw weights over its share of the tiles into
+//     the workspace; group 0 of each sequence writes everything but the
+//     closing token.
+//   k_draw_select (B groups): the tile scan and the scan inside one tile.
+constexpr int NT_DRAW = kDrawRound;
+
 template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_FIN) void k_stochastic_finish(Params p) {
-    __shared__ StochFin<NT_FIN> sm;
-    const int b = blockIdx.x;
-    const int S = p.S;
+__global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
+    constexpr int NT = NT_DRAW;
+    constexpr int NW = NT / 64;
+    constexpr int E = Chunk<DT, VEC>::E;
+    __shared__ StochFin<NT> sm;
+    const int b = blockIdx.x / p.SD;
+    const int sd = blockIdx.x - b * p.SD;
+    const int tid = threadIdx.x;
+    const int k = p.k, V = p.V, S = p.S;
+    const float c = p.c;
     const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
-    for (int r = threadIdx.x; r < p.rows_per_seq; r += NT_FIN) {
+    for (int r = tid; r < p.rows_per_seq; r += NT) {
         float R = -FLT_MAX;
         for (int j = 0; j < S; ++j) R = fmaxf(R, part[(r * S + j) * 2]);
         float Z = 0.0f;
@@ -1074,7 +1109,124 @@ __global__ __launch_bounds__(NT_FIN) void k_stochastic_finish(Params p) {
         sm.Z[r] = Z;
     }
     __syncthreads();
-    finish_stochastic<DT, VEC, NT_FIN>(p, b, sm);
+    const int32_t* x = p.tokens_in + (size_t)b * k;
+    for (int i = tid; i < k; i += NT) {
+        const int xi = x[i];
+        float pi = 0.0f, qi = 0.0f;
+        if (xi >= 0 && xi < V) {
+            const float tv = load_elem<DT>(stoch_row<DT>(p, b, i), xi);
+            const float dv = load_elem<DT>(stoch_row<DT>(p, b, k + 1 + i), xi);
+            pi = fast_exp2(fmaf(tv, c, -sm.R[i])) / sm.Z[i];
+            qi = fast_exp2(fmaf(dv, c, -sm.R[k + 1 + i])) / sm.Z[k + 1 + i];
+        }
+        sm.px[i] = pi;
+        sm.qx[i] = qi;
+        if (p.dbg && sd == 0) {
+            p.dbg[((size_t)b * k + i) * 2] = pi;
+            p.dbg[((size_t)b * k + i) * 2 + 1] = qi;
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const float* u = p.u_accept + (size_t)b * k;
+        int a = k;
+        for (int i = 0; i < k; ++i)
+            if (!(u[i] * sm.qx[i] < sm.px[i])) {
+                a = i;
+                break;
+            }
+        sm.a = a;
+    }
+    __syncthreads();
+    const int a = sm.a;
+    // draw parameters: residual exponents, or the bonus row's reference
+    const float w0 = a < k ? -(sm.R[a] + __log2f(sm.Z[a])) : -sm.R[k];
+    const float w1 = a < k ? -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a])) : 0.0f;
+    const float w2 = -sm.R[a];  // p_a itself, if the residual turns out empty
+    if (sd == 0) {
+        int32_t* out = p.tokens_out + (size_t)b * (k + 1);
+        for (int i = tid; i <= k; i += NT) {
+            if (i < a) out[i] = x[i];
+            else if (i > a) out[i] = -1;
+        }
+        if (tid == 0) {
+            p.accept_len[b] = a;
+            int* m = p.meta + (size_t)b * 4;
+            m[0] = a;
+            m[1] = __float_as_int(w0);
+            m[2] = __float_as_int(w1);
+            m[3] = __float_as_int(w2);
+        }
+    }
+    // this group's tiles of the draw row(s)
+    const Row<DT, VEC> tr(stoch_row<DT>(p, b, a), V);
+    const Row<DT, VEC> dr(stoch_row<DT>(p, b, a < k ? k + 1 + a : a), V);
+    const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
+    const int tps = (g.nt_all + p.SD - 1) / p.SD;
+    const int t0 = sd * tps, t1 = min(g.nt_all, t0 + tps);
+    if (t0 >= t1) return;  // uniform: this group has no tiles
+    for (int t = tid; t < (t1 - t0) * NW; t += NT) sm.tile_part[t] = 0.0f;
+    __syncthreads();
+    const int r0 = t0 * g.m, r1 = min(g.rounds, t1 * g.m);
+    if (a < k) {
+        const ResidualW w{c, w0, w1};
+        if (r0 < r1) cdf_pass_a_rounds<DT, VEC, true, NT>(tr, dr, w, g, r0, r1, t0, sm.tile_part);
+        if (g.ntiles >= t0 && g.ntiles < t1)
+            cdf_trailing<DT, VEC, true, NT>(tr, dr, w, g, sm.tile_part, t0);
+    } else {
+        const TargetW w{c, w0};
+        if (r0 < r1) cdf_pass_a_rounds<DT, VEC, false, NT>(tr, dr, w, g, r0, r1, t0, sm.tile_part);
+        if (g.ntiles >= t0 && g.ntiles < t1)
+            cdf_trailing<DT, VEC, false, NT>(tr, dr, w, g, sm.tile_part, t0);
+    }
+    __syncthreads();
+    float* ts = p.tilesum + (size_t)b * (kMaxTiles + 1);
+    for (int t = tid; t < t1 - t0; t += NT) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += sm.tile_part[t * NW + w];
+        ts[t0 + t] = s;
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
+    constexpr int NT = NT_DRAW;
+    constexpr int NW = NT / 64;
+    constexpr int E = Chunk<DT, VEC>::E;
+    __shared__ StochFin<NT> sm;
+    const int b = blockIdx.x;
+    const int k = p.k, V = p.V;
+    const float c = p.c;
+    const int* m = p.meta + (size_t)b * 4;
+    const int a = m[0];
+    const float w0 = __int_as_float(m[1]), w1 = __int_as_float(m[2]), w2 = __int_as_float(m[3]);
+    const Row<DT, VEC> tr(stoch_row<DT>(p, b, a), V);
+    const Row<DT, VEC> dr(stoch_row<DT>(p, b, a < k ? k + 1 + a : a), V);
+    const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
+    const float* ts = p.tilesum + (size_t)b * (kMaxTiles + 1);
+    for (int t = threadIdx.x; t < g.nt_all * NW; t += NT)
+        sm.tile_part[t] = (t % NW) == 0 ? ts[t / NW] : 0.0f;
+    __syncthreads();
+    const float rr = p.u_sample[b];
+    float total = 0.0f;
+    int y;
+    if (a < k) {
+        const ResidualW w{c, w0, w1};
+        y = cdf_select<DT, VEC, true, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
+                                          sm.sc);
+        if (!(total > 0.0f)) {
+            // p == q to float precision: the residual is empty; draw from p_a.
+            const TargetW tw{c, w2};
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, a), nullptr, V, tw, rr,
+                                                    &total, sm.tile_part, sm.tile_excl, sm.sc);
+        }
+    } else {
+        const TargetW w{c, w0};
+        y = cdf_select<DT, VEC, false, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
+                                           sm.sc);
+    }
+    if (threadIdx.x == 0) p.tokens_out[(size_t)b * (k + 1) + a] = y;
 }
 
 __global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
@@ -1115,7 +1267,9 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     const long long items = (long long)p.B * p.rows_per_seq * p.S;
     int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
     if (e) return e;
-    return launch1(k_stochastic_finish<DT, VEC>, p, p.B, NT_FIN, stream);
+    e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
+    if (e) return e;
+    return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);
 }
 
 template <int DT, bool VEC>
