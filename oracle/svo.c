@@ -231,6 +231,37 @@ static int argmax_row(const void* base, int dtype, int64_t row_off, int V) {
     return best;
 }
 
+/* Greedy verification of one sequence whose first candidate row is at
+ * element offset `base`: G candidates of k+1 rows each (k may be 0: then the
+ * emitted token is just the argmax of row 0). */
+static void greedy_one(const void* target, const int32_t* x, int G, int k, int V,
+                       int64_t stride, int dtype, int64_t base, int32_t* accept_len,
+                       int32_t* out, int32_t* best_cand, int32_t* cand_accept) {
+    int best_c = 0, best_a = -1;
+    for (int c = 0; c < G; ++c) {
+        const int32_t* xc = x + (int64_t)c * k;
+        int64_t row0 = base + (int64_t)c * (k + 1) * stride;
+        int a = k;
+        for (int i = 0; i < k; ++i) {
+            int g = argmax_row(target, dtype, row0 + i * stride, V);
+            if (xc[i] != g) {
+                a = i;
+                break;
+            }
+        }
+        if (cand_accept) cand_accept[c] = a;
+        if (a > best_a) {
+            best_a = a;
+            best_c = c;
+        }
+    }
+    int64_t row0 = base + (int64_t)best_c * (k + 1) * stride;
+    for (int i = 0; i <= best_a; ++i) out[i] = argmax_row(target, dtype, row0 + i * stride, V);
+    for (int i = best_a + 1; i <= k; ++i) out[i] = -1;
+    *accept_len = best_a;
+    if (best_cand) *best_cand = best_c;
+}
+
 int svo_verify_greedy(const void* target, const int32_t* draft_tokens, int B,
                       int G, int k, int V, int64_t row_stride, int dtype,
                       int32_t* accept_len, int32_t* tokens, int32_t* best_cand,
@@ -239,34 +270,120 @@ int svo_verify_greedy(const void* target, const int32_t* draft_tokens, int B,
     if (B < 0 || G < 1 || k < 1 || V < 1 || row_stride < V) return -1;
     if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b)
+        greedy_one(target, draft_tokens + (int64_t)b * G * k, G, k, V, row_stride, dtype,
+                   (int64_t)b * G * (k + 1) * row_stride, accept_len + b,
+                   tokens + (int64_t)b * (k + 1), best_cand ? best_cand + b : NULL,
+                   cand_accept ? cand_accept + (int64_t)b * G : NULL);
+    return 0;
+}
+
+/* Ragged batches: sequence b has k_b = cu[b+1] - cu[b] draft tokens (0 <= k_b
+ * <= k_max) and its rows are packed: target rows cu[b] + b .. cu[b] + b + k_b,
+ * draft rows cu[b] .. cu[b] + k_b - 1; draft tokens and acceptance uniforms
+ * at cu[b] ..; outputs padded to k_max + 1 per sequence.  Each sequence is
+ * verified exactly as a batch of one with its own k (k_b = 0 samples the
+ * first target row). */
+static int ragged_ok(const int32_t* cu, int B, int k_max) {
+    if (cu[0] != 0) return 0;
     for (int b = 0; b < B; ++b) {
-        int best_c = 0, best_a = -1;
-        for (int c = 0; c < G; ++c) {
-            const int32_t* x = draft_tokens + ((int64_t)b * G + c) * k;
-            int64_t base = ((int64_t)b * G + c) * (k + 1);
-            int a = k;
-            for (int i = 0; i < k; ++i) {
-                int g = argmax_row(target, dtype, (base + i) * row_stride, V);
-                if (x[i] != g) {
-                    a = i;
-                    break;
-                }
-            }
-            if (cand_accept) cand_accept[(int64_t)b * G + c] = a;
-            if (a > best_a) {
-                best_a = a;
-                best_c = c;
-            }
+        int kb = cu[b + 1] - cu[b];
+        if (kb < 0 || kb > k_max) return 0;
+    }
+    return 1;
+}
+
+static size_t elem_size(int dtype) { return dtype == SVO_F32 ? 4 : 2; }
+
+int svo_verify_stochastic_ragged(const void* target, const void* draft,
+                                 const int32_t* draft_tokens, const int32_t* cu,
+                                 const float* u_accept, const float* u_sample,
+                                 int B, int k_max, int V, int64_t row_stride,
+                                 int dtype, double temperature,
+                                 int32_t* accept_len, int32_t* tokens,
+                                 double* px, double* qx) {
+    if (!target || !draft || !draft_tokens || !cu || !u_accept || !u_sample ||
+        !accept_len || !tokens)
+        return -1;
+    if (B < 0 || k_max < 0 || V < 1 || row_stride < V) return -1;
+    if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
+    if (!(temperature > 0.0) || !isfinite(temperature)) return -1;
+    if (!ragged_ok(cu, B, k_max)) return -1;
+    const size_t es = elem_size(dtype);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const int kb = cu[b + 1] - cu[b];
+        const int64_t t0 = (int64_t)cu[b] + b, d0 = cu[b];
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        double* q = (double*)malloc(sizeof(double) * (size_t)V);
+        double* w = (double*)malloc(sizeof(double) * (size_t)V);
+        if (!p || !q || !w) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            int32_t* out = tokens + (int64_t)b * (k_max + 1);
+            stochastic_one((const char*)target + t0 * row_stride * es,
+                           (const char*)draft + d0 * row_stride * es, draft_tokens + d0,
+                           u_accept + d0, u_sample[b], 0, kb, V, row_stride, dtype,
+                           temperature, NULL, accept_len + b, out, px ? px + d0 : NULL,
+                           qx ? qx + d0 : NULL, NULL, NULL, p, q, w);
+            for (int i = kb + 1; i <= k_max; ++i) out[i] = -1;
         }
-        int64_t base = ((int64_t)b * G + best_c) * (k + 1);
-        int32_t* out = tokens + (int64_t)b * (k + 1);
-        for (int i = 0; i <= best_a; ++i)
-            out[i] = argmax_row(target, dtype, (base + i) * row_stride, V);
-        for (int i = best_a + 1; i <= k; ++i) out[i] = -1;
-        accept_len[b] = best_a;
-        if (best_cand) best_cand[b] = best_c;
+        free(p);
+        free(q);
+        free(w);
+    }
+    return bad ? -1 : 0;
+}
+
+int svo_verify_greedy_ragged(const void* target, const int32_t* draft_tokens,
+                             const int32_t* cu, int B, int k_max, int V,
+                             int64_t row_stride, int dtype, int32_t* accept_len,
+                             int32_t* tokens) {
+    if (!target || !draft_tokens || !cu || !accept_len || !tokens) return -1;
+    if (B < 0 || k_max < 0 || V < 1 || row_stride < V) return -1;
+    if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
+    if (!ragged_ok(cu, B, k_max)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const int kb = cu[b + 1] - cu[b];
+        int32_t* out = tokens + (int64_t)b * (k_max + 1);
+        greedy_one(target, draft_tokens + cu[b], 1, kb, V, row_stride, dtype,
+                   ((int64_t)cu[b] + b) * row_stride, accept_len + b, out, NULL, NULL);
+        for (int i = kb + 1; i <= k_max; ++i) out[i] = -1;
     }
     return 0;
+}
+
+/* Plain sampling of one token per row: the first token whose cumulative
+ * softmax(row / T) mass exceeds u[b], or (greedy) the row's argmax, lowest
+ * index on ties. */
+int svo_sample(const void* logits, const float* u, int B, int V,
+               int64_t row_stride, int dtype, double temperature, int greedy,
+               int32_t* tokens) {
+    if (!logits || !tokens || (!greedy && !u)) return -1;
+    if (B < 0 || V < 1 || row_stride < V) return -1;
+    if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
+    if (!greedy && (!(temperature > 0.0) || !isfinite(temperature))) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        if (greedy) {
+            tokens[b] = argmax_row(logits, dtype, (int64_t)b * row_stride, V);
+            continue;
+        }
+        double* p = (double*)malloc(sizeof(double) * (size_t)V);
+        if (!p) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        softmax_row(logits, dtype, (int64_t)b * row_stride, V, temperature, p);
+        tokens[b] = inverse_cdf(p, V, (double)u[b], NULL, NULL);
+        free(p);
+    }
+    return bad ? -1 : 0;
 }
 
 int svo_num_threads(void) {

@@ -93,6 +93,31 @@ int svo_verify_greedy(const void* target, const int32_t* draft_tokens, int B,
                       int32_t* accept_len, int32_t* tokens, int32_t* best_cand,
                       int32_t* cand_accept);
 
+/* Ragged batches (sequence b has k_b = cu[b+1] - cu[b] draft tokens,
+ * 0 <= k_b <= k_max, cu[0] = 0): target rows of sequence b are rows
+ * cu[b] + b .. cu[b] + b + k_b, its draft rows cu[b] .. cu[b] + k_b - 1, its
+ * draft tokens and acceptance uniforms entries cu[b] ..; px/qx (nullable)
+ * are [cu[B]]; tokens are [B][k_max + 1].  k_b = 0 samples the first target
+ * row (plain sampling).  Returns -1 on a bad argument or malformed cu. */
+int svo_verify_stochastic_ragged(const void* target, const void* draft,
+                                 const int32_t* draft_tokens, const int32_t* cu,
+                                 const float* u_accept, const float* u_sample,
+                                 int B, int k_max, int V, int64_t row_stride,
+                                 int dtype, double temperature,
+                                 int32_t* accept_len, int32_t* tokens,
+                                 double* px, double* qx);
+
+int svo_verify_greedy_ragged(const void* target, const int32_t* draft_tokens,
+                             const int32_t* cu, int B, int k_max, int V,
+                             int64_t row_stride, int dtype, int32_t* accept_len,
+                             int32_t* tokens);
+
+/* Plain sampling, one token per row b of logits: inverse CDF of
+ * softmax(row / temperature) at u[b], or the argmax when greedy != 0. */
+int svo_sample(const void* logits, const float* u, int B, int V,
+               int64_t row_stride, int dtype, double temperature, int greedy,
+               int32_t* tokens);
+
 /* Number of OpenMP threads the batched entry points use. */
 int svo_num_threads(void);
 

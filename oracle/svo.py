@@ -48,6 +48,13 @@ def _bind(lib):
     lib.svo_emit_cdf.restype = I
     lib.svo_verify_greedy.argtypes = [P, P, I, I, I, I, ctypes.c_int64, I, P, P, P, P]
     lib.svo_verify_greedy.restype = I
+    lib.svo_verify_stochastic_ragged.argtypes = [P, P, P, P, P, P, I, I, I, ctypes.c_int64, I,
+                                                 ctypes.c_double, P, P, P, P]
+    lib.svo_verify_stochastic_ragged.restype = I
+    lib.svo_verify_greedy_ragged.argtypes = [P, P, P, I, I, I, ctypes.c_int64, I, P, P]
+    lib.svo_verify_greedy_ragged.restype = I
+    lib.svo_sample.argtypes = [P, P, I, I, ctypes.c_int64, I, ctypes.c_double, I, P]
+    lib.svo_sample.restype = I
     lib.svo_num_threads.argtypes = []
     lib.svo_num_threads.restype = I
     return lib
@@ -143,6 +150,73 @@ def verify_greedy(target, draft_tokens, *, B, G=1, k, V, row_stride=None, lib=No
     rc = lib.svo_verify_greedy(_ptr(target), _ptr(x), B, G, k, V, row_stride, dt,
                                _ptr(out["accept_len"]), _ptr(out["tokens"]),
                                _ptr(out["best_cand"]), _ptr(out["cand_accept"]))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def verify_stochastic_ragged(target, draft, draft_tokens, cu, u_accept, u_sample, *, k_max, V,
+                             row_stride=None, temperature=1.0, lib=None):
+    """Ragged stochastic verification (see svo.h).  cu: int32 [B+1].  Returns
+    accept_len [B], tokens [B][k_max+1], px, qx [cu[B]]."""
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    dt = _dtype_code(target)
+    row_stride = V if row_stride is None else int(row_stride)
+    cu = _c(cu, np.int32).reshape(-1)
+    B = cu.size - 1
+    n = int(cu[-1])
+    assert target.size >= (n + B) * row_stride and draft.size >= n * row_stride
+    x = _c(draft_tokens, np.int32).reshape(-1)
+    ua = _c(u_accept, np.float32).reshape(-1)
+    us = _c(u_sample, np.float32).reshape(-1)
+    assert x.size >= n and ua.size >= n and us.size == B
+    if n == 0:  # keep every pointer valid
+        x, ua = np.zeros(1, np.int32), np.zeros(1, np.float32)
+    out = dict(accept_len=np.zeros(B, np.int32), tokens=np.zeros((B, k_max + 1), np.int32),
+               px=np.zeros(max(n, 1)), qx=np.zeros(max(n, 1)))
+    d = draft if draft.size else np.zeros(1, draft.dtype)
+    rc = lib.svo_verify_stochastic_ragged(_ptr(target), _ptr(d), _ptr(x), _ptr(cu), _ptr(ua),
+                                          _ptr(us), B, k_max, V, row_stride, dt,
+                                          float(temperature), _ptr(out["accept_len"]),
+                                          _ptr(out["tokens"]), _ptr(out["px"]), _ptr(out["qx"]))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    out["px"], out["qx"] = out["px"][:n], out["qx"][:n]
+    return out
+
+
+def verify_greedy_ragged(target, draft_tokens, cu, *, k_max, V, row_stride=None, lib=None):
+    """Ragged greedy verification (see svo.h).  Returns accept_len [B], tokens
+    [B][k_max+1]."""
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    dt = _dtype_code(target)
+    row_stride = V if row_stride is None else int(row_stride)
+    cu = _c(cu, np.int32).reshape(-1)
+    B = cu.size - 1
+    x = _c(draft_tokens, np.int32).reshape(-1)
+    if x.size == 0:
+        x = np.zeros(1, np.int32)
+    out = dict(accept_len=np.zeros(B, np.int32), tokens=np.zeros((B, k_max + 1), np.int32))
+    rc = lib.svo_verify_greedy_ragged(_ptr(target), _ptr(x), _ptr(cu), B, k_max, V, row_stride,
+                                      dt, _ptr(out["accept_len"]), _ptr(out["tokens"]))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def sample(logits, u, *, B, V, row_stride=None, temperature=1.0, greedy=False, lib=None):
+    """Plain sampling of one token per row (see svo.h).  Returns int32 [B]."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits)
+    dt = _dtype_code(logits)
+    row_stride = V if row_stride is None else int(row_stride)
+    uu = None if u is None else _c(u, np.float32).reshape(-1)
+    out = np.zeros(B, np.int32)
+    rc = lib.svo_sample(_ptr(logits), _ptr(uu), B, V, row_stride, dt, float(temperature),
+                        1 if greedy else 0, _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out

@@ -417,5 +417,69 @@ def pin_invariants(lib):
         assert abs(hi - 1.0) < 1e-12
 
 
+# ------------------------------------------------------- ragged, sampling --
+
+def ragged_batch(rng, B, k_max, V, dtype_f32=True, with_zero=True):
+    kb = rng.integers(0 if with_zero else 1, k_max + 1, size=B)
+    cu = np.concatenate([[0], np.cumsum(kb)]).astype(np.int32)
+    n = int(cu[-1])
+    t = (rng.standard_normal((n + B, V)) * 2).astype(np.float32)
+    d = (rng.standard_normal((max(n, 1), V)) * 2).astype(np.float32)
+    x = rng.integers(0, V, size=max(n, 1)).astype(np.int32)
+    ua = rng.random(max(n, 1)).astype(np.float32)
+    us = rng.random(B).astype(np.float32)
+    return kb, cu, t, d, x, ua, us
+
+
+def pin_ragged_equals_dense(lib):
+    """A ragged batch is each of its sequences verified on its own: sequence
+    b with k_b draft tokens gives what a batch of one with k = k_b gives, and
+    k_b = 0 gives plain sampling of its first target row."""
+    rng = np.random.default_rng(21)
+    for (B, k_max, V, tau) in [(30, 5, 40, 1.0), (17, 3, 7, 0.8), (9, 8, 300, 1.3)]:
+        kb, cu, t, d, x, ua, us = ragged_batch(rng, B, k_max, V)
+        o = svo.verify_stochastic_ragged(t, d, x, cu, ua, us, k_max=k_max, V=V,
+                                         temperature=tau, lib=lib)
+        g = svo.verify_greedy_ragged(t, x, cu, k_max=k_max, V=V, lib=lib)
+        for b in range(B):
+            k = int(kb[b])
+            t0, d0 = int(cu[b]) + b, int(cu[b])
+            tb = t[t0:t0 + k + 1]
+            if k == 0:
+                y = svo.sample(tb, us[b:b + 1], B=1, V=V, temperature=tau, lib=lib)[0]
+                assert o["accept_len"][b] == 0 and o["tokens"][b, 0] == y
+                yg = svo.sample(tb, None, B=1, V=V, greedy=True, lib=lib)[0]
+                assert g["accept_len"][b] == 0 and g["tokens"][b, 0] == yg
+            else:
+                ref = svo.verify_stochastic(tb, d[d0:d0 + k], x[d0:d0 + k], ua[d0:d0 + k],
+                                            us[b:b + 1], B=1, k=k, V=V, temperature=tau,
+                                            lib=lib)
+                assert o["accept_len"][b] == ref["accept_len"][0]
+                assert np.array_equal(o["tokens"][b, :k + 1], ref["tokens"][0])
+                assert np.array_equal(o["px"][d0:d0 + k], ref["px"][0])
+                assert np.array_equal(o["qx"][d0:d0 + k], ref["qx"][0])
+                rg = svo.verify_greedy(tb, x[d0:d0 + k], B=1, k=k, V=V, lib=lib)
+                assert g["accept_len"][b] == rg["accept_len"][0]
+                assert np.array_equal(g["tokens"][b, :k + 1], rg["tokens"][0])
+            assert np.all(o["tokens"][b, k + 1:] == -1) and np.all(g["tokens"][b, k + 1:] == -1)
+
+
+def pin_sample_library(lib):
+    """Plain sampling: numpy.searchsorted(cumsum(softmax(t/T)), u, 'right'),
+    and numpy.argmax (first maximum) when greedy."""
+    rng = np.random.default_rng(22)
+    for (B, V, tau) in [(200, 5, 1.0), (100, 1000, 0.7), (50, 32000, 1.0)]:
+        t = (rng.standard_normal((B, V)) * 3).astype(np.float32)
+        u = rng.random(B).astype(np.float32)
+        y = svo.sample(t, u, B=B, V=V, temperature=tau, lib=lib)
+        p = softmax64(t, tau)
+        for b in range(B):
+            assert y[b] == int(np.searchsorted(np.cumsum(p[b]), float(u[b]), side="right"))
+        ti = rng.integers(-2, 2, size=(B, V)).astype(np.float32)  # ties
+        yg = svo.sample(ti, None, B=B, V=V, greedy=True, lib=lib)
+        assert np.array_equal(yg, np.argmax(ti, axis=1))
+
+
 ALL_PINS = [pin_enumeration, pin_softmax, pin_bonus_searchsorted, pin_onehot_residual,
-            pin_greedy_argmax, pin_greedy_bf16_ties, pin_closed_forms, pin_invariants]
+            pin_greedy_argmax, pin_greedy_bf16_ties, pin_closed_forms, pin_invariants,
+            pin_ragged_equals_dense, pin_sample_library]

@@ -33,8 +33,16 @@ MUTANTS = [
     ("residual_from_target_only", "double d = pa[v] - qa[v];", "double d = pa[v];"),
     ("argmax_last_tie", "if (x > bv) {", "if (x >= bv) {"),
     ("candidate_last_tie", "if (a > best_a) {", "if (a >= best_a) {"),
-    ("greedy_emits_draft", "out[i] = argmax_row(target, dtype, (base + i) * row_stride, V);",
-     "out[i] = i < best_a ? draft_tokens[((int64_t)b * G + best_c) * k + i] : 0;"),
+    ("greedy_emits_draft", "for (int i = 0; i <= best_a; ++i) out[i] = argmax_row(target, dtype, row0 + i * stride, V);",
+     "for (int i = 0; i <= best_a; ++i) out[i] = i < best_a ? x[best_c * k + i] : 0;"),
+    ("ragged_target_offset", "const int64_t t0 = (int64_t)cu[b] + b, d0 = cu[b];",
+     "const int64_t t0 = (int64_t)cu[b], d0 = cu[b];"),
+    ("ragged_greedy_offset", "((int64_t)cu[b] + b) * row_stride, accept_len + b, out, NULL, NULL);",
+     "((int64_t)cu[b]) * row_stride, accept_len + b, out, NULL, NULL);"),
+    ("sample_last_tie_argmax", "tokens[b] = argmax_row(logits, dtype, (int64_t)b * row_stride, V);",
+     "tokens[b] = V - 1 - argmax_row(logits, dtype, (int64_t)b * row_stride, V);"),
+    ("sample_no_temperature", "softmax_row(logits, dtype, (int64_t)b * row_stride, V, temperature, p);",
+     "softmax_row(logits, dtype, (int64_t)b * row_stride, V, 1.0, p);"),
     ("token_row_offset", "return ((int64_t)b * (k + 1) + i) * stride;",
      "return ((int64_t)b * k + i) * stride;"),
     ("softmax_no_max_shift", "prob[v] = exp((logit(base, dtype, row_off + v) - M) / tau);",
