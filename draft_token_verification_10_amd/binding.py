@@ -40,6 +40,13 @@ def load(path: str | None = None):
     lib.sv_verify_stochastic.restype = I
     lib.sv_verify_greedy.argtypes = [P, P, I, I, I, I, I64, I, P, P, P, P, SZ, P]
     lib.sv_verify_greedy.restype = I
+    lib.sv_verify_stochastic_ragged.argtypes = [P, P, P, P, I, P, P, I, I, I, I64, I,
+                                                ctypes.c_float, P, P, P, P, SZ, P]
+    lib.sv_verify_stochastic_ragged.restype = I
+    lib.sv_verify_greedy_ragged.argtypes = [P, P, P, I, I, I, I, I64, I, P, P, P, SZ, P]
+    lib.sv_verify_greedy_ragged.restype = I
+    lib.sv_sample.argtypes = [P, P, I, I, I64, I, ctypes.c_float, I, P, P, SZ, P]
+    lib.sv_sample.restype = I
     lib.sv_workspace_bytes.argtypes = [I, I, I, I]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_status_string.argtypes = [I]
@@ -208,3 +215,119 @@ def sv_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor, *,
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accept_len, tokens, best_cand
+
+
+def _rows_2d(t: torch.Tensor, name: str):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a [rows][V] tensor")
+    return t.shape[0], t.shape[1], _row_stride(t)
+
+
+def sv_verify_stochastic_ragged(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                draft_tokens: torch.Tensor, cu_draft_len: torch.Tensor,
+                                u_accept: torch.Tensor, u_sample: torch.Tensor, k_max: int,
+                                temperature: float = 1.0, *, total_draft: int | None = None,
+                                accept_len=None, tokens=None, dbg_px_qx=None, workspace=None,
+                                stream=None):
+    """Ragged stochastic verification.  target_logits [total+B][V] and
+    draft_logits [total][V] packed rows, draft_tokens int32 [total], cu_draft_len
+    int32 [B+1] (device), u_accept float32 [total], u_sample float32 [B].
+    total_draft defaults to draft_tokens' length.  Returns (accept_len [B],
+    tokens [B][k_max+1])."""
+    _dev(target_logits)
+    nt, V, rs = _rows_2d(target_logits, "target_logits")
+    B = cu_draft_len.numel() - 1
+    total = int(draft_tokens.numel()) if total_draft is None else int(total_draft)
+    if nt < total + B:
+        raise ValueError("target_logits needs total_draft + B rows")
+    _check_i32(cu_draft_len, (B + 1,), "cu_draft_len")
+    if total > 0:
+        _dev(draft_logits)
+        nd, Vd, rsd = _rows_2d(draft_logits, "draft_logits")
+        if Vd != V or rsd != rs or nd < total or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [total_draft][V] like the target rows")
+        _check_i32(draft_tokens, (total,), "draft_tokens")
+        _check_f32(u_accept, (total,), "u_accept")
+    _check_f32(u_sample, (B,), "u_sample")
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, k_max + 1), "tokens")
+    if dbg_px_qx is not None:
+        _check_f32(dbg_px_qx, (total, 2), "dbg_px_qx")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, 1, k_max, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_verify_stochastic_ragged(
+        _ptr(target_logits), _ptr(draft_logits if total > 0 else None),
+        _ptr(draft_tokens if total > 0 else None), _ptr(cu_draft_len), total,
+        _ptr(u_accept if total > 0 else None), _ptr(u_sample), B, k_max, V, rs,
+        _dtype_code(target_logits), float(temperature), _ptr(accept_len), _ptr(tokens),
+        _ptr(dbg_px_qx), _ptr(workspace), _ws_bytes(workspace), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens
+
+
+def sv_verify_greedy_ragged(target_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                            cu_draft_len: torch.Tensor, k_max: int, *,
+                            total_draft: int | None = None, accept_len=None, tokens=None,
+                            workspace=None, stream=None):
+    """Ragged greedy verification (one candidate per sequence).  Returns
+    (accept_len [B], tokens [B][k_max+1])."""
+    _dev(target_logits)
+    nt, V, rs = _rows_2d(target_logits, "target_logits")
+    B = cu_draft_len.numel() - 1
+    total = int(draft_tokens.numel()) if total_draft is None else int(total_draft)
+    if nt < total + B:
+        raise ValueError("target_logits needs total_draft + B rows")
+    _check_i32(cu_draft_len, (B + 1,), "cu_draft_len")
+    if total > 0:
+        _check_i32(draft_tokens, (total,), "draft_tokens")
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, k_max + 1), "tokens")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, 1, k_max, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_verify_greedy_ragged(
+        _ptr(target_logits), _ptr(draft_tokens if total > 0 else None), _ptr(cu_draft_len),
+        total, B, k_max, V, rs, _dtype_code(target_logits), _ptr(accept_len), _ptr(tokens),
+        _ptr(workspace), _ws_bytes(workspace), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens
+
+
+def sv_sample(logits: torch.Tensor, u: torch.Tensor | None, temperature: float = 1.0, *,
+              greedy: bool = False, tokens=None, workspace=None, stream=None):
+    """One token per row of logits [B][V]: inverse CDF of softmax(row/T) at
+    u[b], or the argmax when greedy.  Returns int32 [B]."""
+    _dev(logits)
+    B, V, rs = _rows_2d(logits, "logits")
+    if not greedy:
+        _check_f32(u, (B,), "u")
+    dev = logits.device
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    _check_i32(tokens, (B,), "tokens")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, 1, 0, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_sample(_ptr(logits), _ptr(None if greedy else u), B, V, rs,
+                          _dtype_code(logits), float(temperature), 1 if greedy else 0,
+                          _ptr(tokens), _ptr(workspace), _ws_bytes(workspace),
+                          ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return tokens

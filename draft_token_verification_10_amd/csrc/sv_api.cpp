@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <climits>
+
 #include "sv_internal.h"
 
 namespace {
@@ -23,7 +25,7 @@ int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_shape(int B, int G, int k, int V, int64_t row_stride) {
-    if (B < 0 || G < 1 || k < 1 || V < 1) return SV_ERR_SHAPE;
+    if (B < 0 || G < 1 || k < 0 || V < 1) return SV_ERR_SHAPE;
     if (k > SV_MAX_K || V > kMaxV) return SV_ERR_SHAPE;
     if ((long long)G * (k + 1) > SV_MAX_ROWS_PER_SEQ) return SV_ERR_SHAPE;
     if (row_stride < V) return SV_ERR_SHAPE;
@@ -114,23 +116,30 @@ const char* sv_status_string(int status) {
     }
 }
 
-int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
-                         const int32_t* draft_tokens, const float* u_accept,
-                         const float* u_sample, int B, int k, int V, int64_t row_stride,
-                         int dtype, float temperature, int32_t* accept_len, int32_t* tokens,
-                         float* dbg_px_qx, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the stochastic entry points.  cu == nullptr: dense batch of
+// k draft tokens per sequence; else ragged (k is the maximum).  accept_len
+// may be null only for internal callers (sv_sample).
+int stochastic_impl(const void* target, const void* draft, const int32_t* x, const int32_t* cu,
+                    long long total_draft, const float* ua, const float* us, int B, int k, int V,
+                    int64_t row_stride, int dtype, float temperature, int32_t* accept_len,
+                    int32_t* tokens, float* dbg, void* workspace, size_t workspace_bytes,
+                    void* stream) {
     int st = check_shape(B, 1, k, V, row_stride);
     if (st != SV_OK) return st;
+    if (cu && (total_draft < 0 || total_draft > INT32_MAX)) return SV_ERR_SHAPE;
     if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
     const double c = 1.4426950408889634 / (double)temperature;
     if (!(temperature > 0.0f) || !isfinite(temperature) || !isfinite((float)c))
         return SV_ERR_TEMPERATURE;
     if (B == 0) return SV_OK;
-    if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
-        !accept_len || !tokens)
-        return SV_ERR_NULL;
-    const void* bases[2] = {target_logits, draft_logits};
+    const bool drafts = cu ? total_draft > 0 : k > 0;
+    if (!target || !us || !tokens) return SV_ERR_NULL;
+    if (drafts && (!draft || !x || !ua)) return SV_ERR_NULL;
+    const void* bases[2] = {target, drafts ? draft : target};
     Plan pl;
     st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, true, bases, 2, &pl);
     if (st != SV_OK) return st;
@@ -138,15 +147,15 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
     if (st != SV_OK) return st;
 
     sv::Params p = {};
-    p.target = target_logits;
-    p.draft = draft_logits;
-    p.tokens_in = draft_tokens;
-    p.u_accept = u_accept;
-    p.u_sample = u_sample;
+    p.target = target;
+    p.draft = draft;
+    p.tokens_in = x;
+    p.u_accept = ua;
+    p.u_sample = us;
     p.accept_len = accept_len;
     p.tokens_out = tokens;
     p.best_cand = nullptr;
-    p.dbg = dbg_px_qx;
+    p.dbg = dbg;
     p.part = static_cast<float*>(workspace);
     if (!pl.seq) {
         char* w = static_cast<char*>(workspace) + sv::part_bytes(B, pl.rows_per_seq, pl.S);
@@ -154,6 +163,8 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
         p.meta = reinterpret_cast<int*>(w + sv::tilesum_bytes(B));
     }
     p.SD = pl.SD;
+    p.cu = cu;
+    p.total_draft = total_draft;
     p.row_stride = row_stride;
     p.B = B;
     p.G = 1;
@@ -166,16 +177,19 @@ int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
     return sv::launch_stochastic(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
 }
 
-int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int G,
-                     int k, int V, int64_t row_stride, int dtype, int32_t* accept_len,
-                     int32_t* tokens, int32_t* best_cand, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+// Shared body of the greedy entry points (cu as above; ragged means G = 1).
+int greedy_impl(const void* target, const int32_t* x, const int32_t* cu, long long total_draft,
+                int B, int G, int k, int V, int64_t row_stride, int dtype, int32_t* accept_len,
+                int32_t* tokens, int32_t* best_cand, void* workspace, size_t workspace_bytes,
+                void* stream) {
     int st = check_shape(B, G, k, V, row_stride);
     if (st != SV_OK) return st;
+    if (cu && (G != 1 || total_draft < 0 || total_draft > INT32_MAX)) return SV_ERR_SHAPE;
     if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
     if (B == 0) return SV_OK;
-    if (!target_logits || !draft_tokens || !accept_len || !tokens) return SV_ERR_NULL;
-    const void* bases[1] = {target_logits};
+    const bool drafts = cu ? total_draft > 0 : k > 0;
+    if (!target || !tokens || (drafts && !x)) return SV_ERR_NULL;
+    const void* bases[1] = {target};
     Plan pl;
     st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, false, bases, 1, &pl);
     if (st != SV_OK) return st;
@@ -183,13 +197,15 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     if (st != SV_OK) return st;
 
     sv::Params p = {};
-    p.target = target_logits;
+    p.target = target;
     p.draft = nullptr;
-    p.tokens_in = draft_tokens;
+    p.tokens_in = x;
     p.accept_len = accept_len;
     p.tokens_out = tokens;
     p.best_cand = best_cand;
     p.part = static_cast<float*>(workspace);
+    p.cu = cu;
+    p.total_draft = total_draft;
     p.row_stride = row_stride;
     p.B = B;
     p.G = G;
@@ -200,6 +216,69 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int
     p.slice_len = pl.slice_len;
     p.c = 0.0f;
     return sv::launch_greedy(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
+                         const int32_t* draft_tokens, const float* u_accept,
+                         const float* u_sample, int B, int k, int V, int64_t row_stride,
+                         int dtype, float temperature, int32_t* accept_len, int32_t* tokens,
+                         float* dbg_px_qx, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (B > 0 && !accept_len) return SV_ERR_NULL;
+    return stochastic_impl(target_logits, draft_logits, draft_tokens, nullptr, 0, u_accept,
+                           u_sample, B, k, V, row_stride, dtype, temperature, accept_len, tokens,
+                           dbg_px_qx, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* cu_draft_len,
+                                int total_draft, const float* u_accept, const float* u_sample,
+                                int B, int k_max, int V, int64_t row_stride, int dtype,
+                                float temperature, int32_t* accept_len, int32_t* tokens,
+                                float* dbg_px_qx, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (B > 0 && (!accept_len || !cu_draft_len)) return SV_ERR_NULL;
+    if (total_draft < 0) return SV_ERR_SHAPE;
+    return stochastic_impl(target_logits, draft_logits, draft_tokens, cu_draft_len, total_draft,
+                           u_accept, u_sample,
+                           B, k_max, V, row_stride, dtype, temperature, accept_len, tokens,
+                           dbg_px_qx, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int G,
+                     int k, int V, int64_t row_stride, int dtype, int32_t* accept_len,
+                     int32_t* tokens, int32_t* best_cand, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (B > 0 && !accept_len) return SV_ERR_NULL;
+    return greedy_impl(target_logits, draft_tokens, nullptr, 0, B, G, k, V, row_stride, dtype,
+                       accept_len, tokens, best_cand, workspace, workspace_bytes, stream);
+}
+
+int sv_verify_greedy_ragged(const void* target_logits, const int32_t* draft_tokens,
+                            const int32_t* cu_draft_len, int total_draft, int B, int k_max,
+                            int V, int64_t row_stride, int dtype, int32_t* accept_len,
+                            int32_t* tokens, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    if (B > 0 && (!accept_len || !cu_draft_len)) return SV_ERR_NULL;
+    if (total_draft < 0) return SV_ERR_SHAPE;
+    return greedy_impl(target_logits, draft_tokens, cu_draft_len, total_draft, B, 1, k_max, V,
+                       row_stride, dtype, accept_len, tokens, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+int sv_sample(const void* logits, const float* u, int B, int V, int64_t row_stride, int dtype,
+              float temperature, int greedy, int32_t* tokens, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    if (greedy)
+        return greedy_impl(logits, nullptr, nullptr, 0, B, 1, 0, V, row_stride, dtype, nullptr,
+                           tokens, nullptr, workspace, workspace_bytes, stream);
+    return stochastic_impl(logits, nullptr, nullptr, nullptr, 0, nullptr, u, B, 0, V, row_stride,
+                           dtype, temperature, nullptr, tokens, nullptr, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

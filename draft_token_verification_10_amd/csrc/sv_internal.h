@@ -95,8 +95,10 @@ struct Params {
     float* tilesum;       // row-split stochastic: [B][kMaxTiles + 1]
     int* meta;            // row-split stochastic: [B][4] draw parameters
     int SD;               // row-split stochastic: draw workgroups per sequence
+    const int32_t* cu;    // ragged batches: cumulative draft lengths [B+1], else null
+    long long total_draft;  // ragged batches: draft rows in the buffers
     long long row_stride; // elements
-    int B, G, k, V;
+    int B, G, k, V;       // k: draft tokens per sequence (ragged: the maximum)
     int rows_per_seq;     // stochastic 2k+1, greedy G(k+1)
     int S;                // row-split: slices per row
     int slice_len;        // row-split: elements per slice

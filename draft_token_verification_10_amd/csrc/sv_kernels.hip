@@ -653,20 +653,50 @@ struct TargetW {
 // ------------------------------------------------------------------------
 // Finishing a sequence.
 
-template <int DT>
-__device__ __forceinline__ const char* stoch_row(const Params& p, int b, int r) {
-    const size_t eb = elem_bytes<DT>();
-    if (r <= p.k)
-        return static_cast<const char*>(p.target) +
-               ((size_t)b * (p.k + 1) + r) * (size_t)p.row_stride * eb;
-    return static_cast<const char*>(p.draft) +
-           ((size_t)b * p.k + (r - p.k - 1)) * (size_t)p.row_stride * eb;
+// A sequence's place in the batch: its draft-token count k, its first
+// target row t0 and its first draft row / draft-token index d0.  Dense
+// batches: the same k for every sequence (G candidate blocks in greedy
+// mode); ragged batches: k_b = cu[b+1] - cu[b] with rows packed (target rows
+// cu[b] + b .., draft rows cu[b] ..), clamped so that a malformed cu can
+// never address outside buffers of total_draft draft rows.
+struct Seq {
+    int k;
+    long long t0, d0;
+};
+
+__device__ __forceinline__ Seq seq_of(const Params& p, int b) {
+    Seq s;
+    if (p.cu) {
+        const long long tot = p.total_draft;
+        long long kb = (long long)p.cu[b + 1] - p.cu[b];
+        kb = kb < 0 ? 0 : (kb > p.k ? p.k : kb);
+        if (kb > tot) kb = tot;
+        long long d0 = p.cu[b];
+        d0 = d0 < 0 ? 0 : (d0 > tot - kb ? tot - kb : d0);
+        s.k = (int)kb;
+        s.d0 = d0;
+        s.t0 = d0 + b;
+    } else {
+        s.k = p.k;
+        s.d0 = (long long)b * p.G * p.k;
+        s.t0 = (long long)b * p.G * (p.k + 1);
+    }
+    return s;
 }
 
+// Row r of a stochastic sequence: target rows 0..k, then draft rows.
 template <int DT>
-__device__ __forceinline__ const char* greedy_row(const Params& p, int b, int r) {
+__device__ __forceinline__ const char* stoch_row(const Params& p, const Seq& s, int r) {
+    const size_t rb = (size_t)p.row_stride * elem_bytes<DT>();
+    if (r <= s.k) return static_cast<const char*>(p.target) + (size_t)(s.t0 + r) * rb;
+    return static_cast<const char*>(p.draft) + (size_t)(s.d0 + (r - s.k - 1)) * rb;
+}
+
+// Row r of a greedy sequence (candidate c's rows are c(k+1) .. c(k+1)+k).
+template <int DT>
+__device__ __forceinline__ const char* greedy_row(const Params& p, const Seq& s, int r) {
     return static_cast<const char*>(p.target) +
-           ((size_t)b * p.rows_per_seq + r) * (size_t)p.row_stride * elem_bytes<DT>();
+           (size_t)(s.t0 + r) * (size_t)p.row_stride * elem_bytes<DT>();
 }
 
 template <int NT>
@@ -683,29 +713,29 @@ struct StochFin {
 
 // Needs R[], Z[] of every row of sequence b in LDS (after a barrier).
 template <int DT, bool VEC, int NT>
-__device__ void finish_stochastic(const Params& p, int b, StochFin<NT>& sm) {
+__device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin<NT>& sm) {
     const int tid = threadIdx.x;
-    const int k = p.k, V = p.V;
-    const int32_t* x = p.tokens_in + (size_t)b * k;
+    const int k = s.k, V = p.V;
+    const int32_t* x = p.tokens_in + s.d0;
     for (int i = tid; i < k; i += NT) {
         const int xi = x[i];
         float pi = 0.0f, qi = 0.0f;
         if (xi >= 0 && xi < V) {
-            const float tv = load_elem<DT>(stoch_row<DT>(p, b, i), xi);
-            const float dv = load_elem<DT>(stoch_row<DT>(p, b, k + 1 + i), xi);
+            const float tv = load_elem<DT>(stoch_row<DT>(p, s, i), xi);
+            const float dv = load_elem<DT>(stoch_row<DT>(p, s, k + 1 + i), xi);
             pi = fast_exp2(fmaf(tv, p.c, -sm.R[i])) / sm.Z[i];
             qi = fast_exp2(fmaf(dv, p.c, -sm.R[k + 1 + i])) / sm.Z[k + 1 + i];
         }
         sm.px[i] = pi;
         sm.qx[i] = qi;
         if (p.dbg) {
-            p.dbg[((size_t)b * k + i) * 2] = pi;
-            p.dbg[((size_t)b * k + i) * 2 + 1] = qi;
+            p.dbg[(s.d0 + i) * 2] = pi;
+            p.dbg[(s.d0 + i) * 2 + 1] = qi;
         }
     }
     __syncthreads();
     if (tid == 0) {
-        const float* u = p.u_accept + (size_t)b * k;
+        const float* u = p.u_accept + s.d0;
         int a = k;
         for (int i = 0; i < k; ++i)
             if (!(u[i] * sm.qx[i] < sm.px[i])) {
@@ -716,17 +746,17 @@ __device__ void finish_stochastic(const Params& p, int b, StochFin<NT>& sm) {
     }
     __syncthreads();
     const int a = sm.a;
-    int32_t* out = p.tokens_out + (size_t)b * (k + 1);
-    for (int i = tid; i <= k; i += NT) {
+    int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
+    for (int i = tid; i <= p.k; i += NT) {
         if (i < a) out[i] = x[i];
         else if (i > a) out[i] = -1;
     }
     const float rr = p.u_sample[b];
-    const char* trow = stoch_row<DT>(p, b, a);
+    const char* trow = stoch_row<DT>(p, s, a);
     float total;
     int y;
     if (a < k) {
-        const char* drow = stoch_row<DT>(p, b, k + 1 + a);
+        const char* drow = stoch_row<DT>(p, s, k + 1 + a);
         const ResidualW w{p.c, -(sm.R[a] + __log2f(sm.Z[a])),
                           -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a]))};
         y = inverse_cdf_row<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.tile_part,
@@ -744,7 +774,7 @@ __device__ void finish_stochastic(const Params& p, int b, StochFin<NT>& sm) {
     }
     if (tid == 0) {
         out[a] = y;
-        p.accept_len[b] = a;
+        if (p.accept_len) p.accept_len[b] = a;
     }
 }
 
@@ -759,10 +789,10 @@ struct GreedyFin {
 
 // Needs g[] of every row of sequence b in LDS (after a barrier).
 template <int NT>
-__device__ void finish_greedy(const Params& p, int b, GreedyFin<NT>& sm) {
+__device__ void finish_greedy(const Params& p, int b, const Seq& s, GreedyFin<NT>& sm) {
     const int tid = threadIdx.x;
-    const int k = p.k, G = p.G;
-    const int32_t* x = p.tokens_in + (size_t)b * G * k;
+    const int k = s.k, G = p.G;
+    const int32_t* x = p.tokens_in + s.d0;
     for (int c = tid; c < G; c += NT) {
         int a = k;
         for (int i = 0; i < k; ++i)
@@ -782,13 +812,13 @@ __device__ void finish_greedy(const Params& p, int b, GreedyFin<NT>& sm) {
             }
         sm.a = ba;
         sm.c = bc;
-        p.accept_len[b] = ba;
+        if (p.accept_len) p.accept_len[b] = ba;
         if (p.best_cand) p.best_cand[b] = bc;
     }
     __syncthreads();
     const int a = sm.a, bc = sm.c;
-    int32_t* out = p.tokens_out + (size_t)b * (k + 1);
-    for (int i = tid; i <= k; i += NT) out[i] = i <= a ? sm.g[bc * (k + 1) + i] : -1;
+    int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
+    for (int i = tid; i <= p.k; i += NT) out[i] = i <= a ? sm.g[bc * (k + 1) + i] : -1;
 }
 
 // ------------------------------------------------------------------------
@@ -818,7 +848,8 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
     __shared__ StochSeqSmem sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int k = p.k;
+    const Seq sq = seq_of(p, b);
+    const int k = sq.k;
     const int rows = 2 * k + 1;
     // Target row k first, then the pairs from position k-1 down to 0, so the
     // rows a rejection most often lands on are the freshest in cache when
@@ -826,7 +857,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
     for (int j = 0; j < rows; ++j) {
         const int i = k - (j + 1) / 2;
         const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
-        const Row<DT, VEC> row(stoch_row<DT>(p, b, r), p.V);
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, r), p.V);
         SoftAcc acc;
         if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT_SEQ, true>(row, p.c, acc);
         else stream_softmax<DT, VEC, NT_SEQ>(row, p.c, acc);
@@ -849,7 +880,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
         sm.fin.Z[r] = Z;
     }
     __syncthreads();
-    finish_stochastic<DT, VEC, NT_SEQ>(p, b, sm.fin);
+    finish_stochastic<DT, VEC, NT_SEQ>(p, b, sq, sm.fin);
 }
 
 // Early-exit variant, used when no per-position diagnostics are asked for:
@@ -874,9 +905,10 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
     __shared__ StochExitSmem sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int k = p.k, V = p.V;
+    const Seq sq = seq_of(p, b);
+    const int k = sq.k, V = p.V;
     const float c = p.c;
-    const int32_t* x = p.tokens_in + (size_t)b * k;
+    const int32_t* x = p.tokens_in + sq.d0;
     // Wave 0 gathers the tokens, uniforms and the logits at the tokens (lane
     // i: position i) while it streams the first row; the first barrier
     // publishes them.
@@ -885,7 +917,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
     float gu = 0.0f, gt = 0.0f, gd = 0.0f;
     if (gather) {
         gx = x[lane];
-        gu = p.u_accept[(size_t)b * k + lane];
+        gu = p.u_accept[sq.d0 + lane];
     }
     int a = k;
     float Rt = 0.0f, Zt = 1.0f, Rd = 0.0f, Zd = 1.0f;
@@ -893,7 +925,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
         float* wR = sm.wR + (i & 1) * 2 * NW;
         float* wZ = sm.wZ + (i & 1) * 2 * NW;
         for (int half = 0; half < 2; ++half) {
-            const Row<DT, VEC> row(stoch_row<DT>(p, b, half == 0 ? i : k + 1 + i), V);
+            const Row<DT, VEC> row(stoch_row<DT>(p, sq, half == 0 ? i : k + 1 + i), V);
             SoftAcc acc;
             stream_softmax<DT, VEC, NT>(row, c, acc);
             float R, Z;
@@ -903,8 +935,8 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
                 wZ[half * NW + wave] = Z;
             }
             if (i == 0 && half == 0 && gather && gx >= 0 && gx < V) {
-                gt = load_elem<DT>(stoch_row<DT>(p, b, lane), gx);
-                gd = load_elem<DT>(stoch_row<DT>(p, b, k + 1 + lane), gx);
+                gt = load_elem<DT>(stoch_row<DT>(p, sq, lane), gx);
+                gd = load_elem<DT>(stoch_row<DT>(p, sq, k + 1 + lane), gx);
             }
         }
         if (i == 0 && gather) {
@@ -929,8 +961,8 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
             break;
         }
     }
-    int32_t* out = p.tokens_out + (size_t)b * (k + 1);
-    for (int i = tid; i <= k; i += NT) {
+    int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
+    for (int i = tid; i <= p.k; i += NT) {
         if (i < a) out[i] = x[i];
         else if (i > a) out[i] = -1;
     }
@@ -939,19 +971,19 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
     int y;
     if (a < k) {
         const ResidualW w{c, -(Rt + __log2f(Zt)), -(Rd + __log2f(Zd))};
-        y = inverse_cdf_row<DT, VEC, true, NT>(stoch_row<DT>(p, b, a), stoch_row<DT>(p, b, k + 1 + a),
+        y = inverse_cdf_row<DT, VEC, true, NT>(stoch_row<DT>(p, sq, a), stoch_row<DT>(p, sq, k + 1 + a),
                                                V, w, rr, &total, sm.fin.tile_part,
                                                sm.fin.tile_excl, sm.fin.sc);
         if (!(total > 0.0f)) {
             // p == q to float precision: the residual is empty; draw from p_a.
             const TargetW tw{c, -Rt};
-            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, a), nullptr, V, tw, rr,
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw, rr,
                                                     &total, sm.fin.tile_part, sm.fin.tile_excl,
                                                     sm.fin.sc);
         }
     } else {
         // every draft token accepted: the bonus token from row k
-        const Row<DT, VEC> row(stoch_row<DT>(p, b, k), V);
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
         SoftAcc acc;
         stream_softmax<DT, VEC, NT>(row, c, acc);
         float R, Z;
@@ -965,12 +997,12 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
         merge_row<NW>(sm.wR + (k & 1) * 2 * NW, sm.wZ + (k & 1) * 2 * NW, 0, Rk, Zk);
         (void)Zk;
         const TargetW tw{c, -Rk};
-        y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, k), nullptr, V, tw, rr, &total,
+        y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, k), nullptr, V, tw, rr, &total,
                                                 sm.fin.tile_part, sm.fin.tile_excl, sm.fin.sc);
     }
     if (tid == 0) {
         out[a] = y;
-        p.accept_len[b] = a;
+        if (p.accept_len) p.accept_len[b] = a;
     }
 }
 
@@ -986,9 +1018,10 @@ __global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
     __shared__ GreedySeqSmem sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rows = p.rows_per_seq;  // k+1 (one candidate)
+    const Seq sq = seq_of(p, b);
+    const int rows = sq.k + 1;  // one candidate
     for (int r = 0; r < rows; ++r) {
-        const Row<DT, VEC> row(greedy_row<DT>(p, b, r), p.V);
+        const Row<DT, VEC> row(greedy_row<DT>(p, sq, r), p.V);
         ArgAcc acc;
         stream_argmax<DT, VEC, NT_SEQ>(row, acc);
         wave_argmax(acc.best, acc.pos);
@@ -1006,11 +1039,11 @@ __global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
                 best = sm.wbest[r * NW + w];
                 pos = sm.wpos[r * NW + w];
             }
-        const Row<DT, VEC> row(greedy_row<DT>(p, b, r), p.V);
+        const Row<DT, VEC> row(greedy_row<DT>(p, sq, r), p.V);
         sm.fin.g[r] = argmax_refine(row, best, pos);
     }
     __syncthreads();
-    finish_greedy<NT_SEQ>(p, b, sm.fin);
+    finish_greedy<NT_SEQ>(p, b, sq, sm.fin);
 }
 
 // ------------------------------------------------------------------------
@@ -1026,10 +1059,12 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
     const int item = blockIdx.x - b * per_seq;
     const int r = item / p.S;
     const int s = item - r * p.S;
+    const Seq sq = seq_of(p, b);
+    if (r >= (STOCH ? 2 * sq.k + 1 : p.G * (sq.k + 1))) return;  // row absent (ragged)
     const int v0 = s * p.slice_len;
     const int v1 = min(p.V, v0 + p.slice_len);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const char* rp = STOCH ? stoch_row<DT>(p, b, r) : greedy_row<DT>(p, b, r);
+    const char* rp = STOCH ? stoch_row<DT>(p, sq, r) : greedy_row<DT>(p, sq, r);
     const Row<DT, VEC> row(rp + (size_t)v0 * elem_bytes<DT>(), v1 - v0);
     float* dst = p.part + ((size_t)b * per_seq + item) * 2;
     if (STOCH) {
@@ -1096,10 +1131,11 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     const int b = blockIdx.x / p.SD;
     const int sd = blockIdx.x - b * p.SD;
     const int tid = threadIdx.x;
-    const int k = p.k, V = p.V, S = p.S;
+    const Seq sq = seq_of(p, b);
+    const int k = sq.k, V = p.V, S = p.S;
     const float c = p.c;
     const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
-    for (int r = tid; r < p.rows_per_seq; r += NT) {
+    for (int r = tid; r < 2 * k + 1; r += NT) {
         float R = -FLT_MAX;
         for (int j = 0; j < S; ++j) R = fmaxf(R, part[(r * S + j) * 2]);
         float Z = 0.0f;
@@ -1109,26 +1145,26 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
         sm.Z[r] = Z;
     }
     __syncthreads();
-    const int32_t* x = p.tokens_in + (size_t)b * k;
+    const int32_t* x = p.tokens_in + sq.d0;
     for (int i = tid; i < k; i += NT) {
         const int xi = x[i];
         float pi = 0.0f, qi = 0.0f;
         if (xi >= 0 && xi < V) {
-            const float tv = load_elem<DT>(stoch_row<DT>(p, b, i), xi);
-            const float dv = load_elem<DT>(stoch_row<DT>(p, b, k + 1 + i), xi);
+            const float tv = load_elem<DT>(stoch_row<DT>(p, sq, i), xi);
+            const float dv = load_elem<DT>(stoch_row<DT>(p, sq, k + 1 + i), xi);
             pi = fast_exp2(fmaf(tv, c, -sm.R[i])) / sm.Z[i];
             qi = fast_exp2(fmaf(dv, c, -sm.R[k + 1 + i])) / sm.Z[k + 1 + i];
         }
         sm.px[i] = pi;
         sm.qx[i] = qi;
         if (p.dbg && sd == 0) {
-            p.dbg[((size_t)b * k + i) * 2] = pi;
-            p.dbg[((size_t)b * k + i) * 2 + 1] = qi;
+            p.dbg[(sq.d0 + i) * 2] = pi;
+            p.dbg[(sq.d0 + i) * 2 + 1] = qi;
         }
     }
     __syncthreads();
     if (tid == 0) {
-        const float* u = p.u_accept + (size_t)b * k;
+        const float* u = p.u_accept + sq.d0;
         int a = k;
         for (int i = 0; i < k; ++i)
             if (!(u[i] * sm.qx[i] < sm.px[i])) {
@@ -1144,13 +1180,13 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     const float w1 = a < k ? -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a])) : 0.0f;
     const float w2 = -sm.R[a];  // p_a itself, if the residual turns out empty
     if (sd == 0) {
-        int32_t* out = p.tokens_out + (size_t)b * (k + 1);
-        for (int i = tid; i <= k; i += NT) {
+        int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
+        for (int i = tid; i <= p.k; i += NT) {
             if (i < a) out[i] = x[i];
             else if (i > a) out[i] = -1;
         }
         if (tid == 0) {
-            p.accept_len[b] = a;
+            if (p.accept_len) p.accept_len[b] = a;
             int* m = p.meta + (size_t)b * 4;
             m[0] = a;
             m[1] = __float_as_int(w0);
@@ -1159,8 +1195,8 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
         }
     }
     // this group's tiles of the draw row(s)
-    const Row<DT, VEC> tr(stoch_row<DT>(p, b, a), V);
-    const Row<DT, VEC> dr(stoch_row<DT>(p, b, a < k ? k + 1 + a : a), V);
+    const Row<DT, VEC> tr(stoch_row<DT>(p, sq, a), V);
+    const Row<DT, VEC> dr(stoch_row<DT>(p, sq, a < k ? k + 1 + a : a), V);
     const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
     const int tps = (g.nt_all + p.SD - 1) / p.SD;
     const int t0 = sd * tps, t1 = min(g.nt_all, t0 + tps);
@@ -1196,13 +1232,14 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     constexpr int E = Chunk<DT, VEC>::E;
     __shared__ StochFin<NT> sm;
     const int b = blockIdx.x;
-    const int k = p.k, V = p.V;
+    const Seq sq = seq_of(p, b);
+    const int k = sq.k, V = p.V;
     const float c = p.c;
     const int* m = p.meta + (size_t)b * 4;
     const int a = m[0];
     const float w0 = __int_as_float(m[1]), w1 = __int_as_float(m[2]), w2 = __int_as_float(m[3]);
-    const Row<DT, VEC> tr(stoch_row<DT>(p, b, a), V);
-    const Row<DT, VEC> dr(stoch_row<DT>(p, b, a < k ? k + 1 + a : a), V);
+    const Row<DT, VEC> tr(stoch_row<DT>(p, sq, a), V);
+    const Row<DT, VEC> dr(stoch_row<DT>(p, sq, a < k ? k + 1 + a : a), V);
     const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
     const float* ts = p.tilesum + (size_t)b * (kMaxTiles + 1);
     for (int t = threadIdx.x; t < g.nt_all * NW; t += NT)
@@ -1218,7 +1255,7 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
         if (!(total > 0.0f)) {
             // p == q to float precision: the residual is empty; draw from p_a.
             const TargetW tw{c, w2};
-            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, b, a), nullptr, V, tw, rr,
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw, rr,
                                                     &total, sm.tile_part, sm.tile_excl, sm.sc);
         }
     } else {
@@ -1226,15 +1263,16 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
         y = cdf_select<DT, VEC, false, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
                                            sm.sc);
     }
-    if (threadIdx.x == 0) p.tokens_out[(size_t)b * (k + 1) + a] = y;
+    if (threadIdx.x == 0) p.tokens_out[(size_t)b * (p.k + 1) + a] = y;
 }
 
 __global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
     __shared__ GreedyFin<NT_FIN> sm;
     const int b = blockIdx.x;
     const int S = p.S;
+    const Seq sq = seq_of(p, b);
     const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
-    for (int r = threadIdx.x; r < p.rows_per_seq; r += NT_FIN) {
+    for (int r = threadIdx.x; r < p.G * (sq.k + 1); r += NT_FIN) {
         float best = part[(r * S) * 2];
         int idx = __float_as_int(part[(r * S) * 2 + 1]);
         for (int j = 1; j < S; ++j) {
@@ -1247,7 +1285,7 @@ __global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
         sm.g[r] = idx;
     }
     __syncthreads();
-    finish_greedy<NT_FIN>(p, b, sm);
+    finish_greedy<NT_FIN>(p, b, sq, sm);
 }
 
 // ------------------------------------------------------------------------

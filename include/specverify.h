@@ -88,7 +88,7 @@ extern "C" {
 /* Status codes. */
 #define SV_OK 0
 #define SV_ERR_NULL (-1)        /* a required pointer is NULL               */
-#define SV_ERR_SHAPE (-2)       /* B < 0, G/k/V < 1, k > SV_MAX_K, G*(k+1) > */
+#define SV_ERR_SHAPE (-2)       /* B < 0, k < 0, G/V < 1, k > SV_MAX_K, G*(k+1) > */
                                 /* SV_MAX_ROWS_PER_SEQ, row_stride < V, or   */
                                 /* the launch grid would be too large        */
 #define SV_ERR_DTYPE (-3)       /* dtype is not SV_DTYPE_F32/SV_DTYPE_BF16  */
@@ -117,7 +117,9 @@ extern "C" {
  *   tokens         out int32 [B][k+1]: x_0..x_{a-1}, the extra token, then -1
  *   dbg_px_qx      optional out float [B][k][2]: p_i(x_i), q_i(x_i) for every
  *                  position (NULL to skip)
- * B == 0 is a no-op that returns SV_OK.
+ * B == 0 is a no-op that returns SV_OK.  k = 0 is allowed (no draft tokens:
+ * the one emitted token is sampled from target row 0; draft_logits,
+ * draft_tokens and u_accept may then be NULL).
  *
  * Rows after a sequence's first rejection cannot change accept_len or
  * tokens.  Without dbg_px_qx, a batch large enough to give every sequence its
@@ -149,8 +151,60 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
                      int32_t* accept_len, int32_t* tokens, int32_t* best_cand,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes that suffice for either entry point at this shape
- * (G = 1 for stochastic calls).  Returns 0 for an invalid shape. */
+/*
+ * Ragged batches: sequence b carries k_b = cu_draft_len[b+1] - cu_draft_len[b]
+ * draft tokens, 0 <= k_b <= k_max, cu_draft_len[0] = 0 (cumulative lengths,
+ * int32 [B+1], device memory), total_draft = cu_draft_len[B] (known to the
+ * caller, who sized the buffers).  Rows are packed: target rows of sequence b
+ * are rows cu[b] + b .. cu[b] + b + k_b of target_logits (total_draft + B
+ * rows), its draft rows cu[b] .. cu[b] + k_b - 1 of draft_logits
+ * (total_draft rows); draft_tokens and u_accept hold total_draft entries at
+ * cu[b] ..; dbg_px_qx is [total_draft][2].  Outputs keep the dense shapes:
+ * accept_len [B], tokens [B][k_max + 1] (-1 after each sequence's extra
+ * token).  A sequence with k_b = 0 just samples its one target row.  Draft
+ * lengths that change per sequence and per step are what Novita's blog
+ * describes in its section "Метод реализации" (the number of candidates is
+ * steered by an adaptive probability threshold; its Fig. 1 shows the draft
+ * length varying), and aidevelopers.cz reports that the gain depends on the
+ * draft length.  Each sequence is verified exactly as a dense batch of one with its
+ * own k would be.  Malformed cu_draft_len values cannot make the library
+ * read outside buffers of the stated sizes (they are clamped on the device),
+ * but give undefined results.  draft_logits, draft_tokens and u_accept may
+ * be NULL when total_draft == 0.  Workspace: sv_workspace_bytes(B, 1, k_max, V).
+ */
+int sv_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* cu_draft_len,
+                                int total_draft, const float* u_accept,
+                                const float* u_sample, int B, int k_max, int V,
+                                int64_t row_stride, int dtype, float temperature,
+                                int32_t* accept_len, int32_t* tokens, float* dbg_px_qx,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+int sv_verify_greedy_ragged(const void* target_logits, const int32_t* draft_tokens,
+                            const int32_t* cu_draft_len, int total_draft, int B, int k_max,
+                            int V, int64_t row_stride, int dtype, int32_t* accept_len,
+                            int32_t* tokens, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Plain sampling of one token per row -- the step the drafter and the prefill
+ * take before verification (Perplexity, section "Cieľ-Návrh": at prefill the
+ * target logits are sampled at once; the draft samples one token per step).
+ *   logits   [B] rows of V logits (row_stride, dtype as above)
+ *   u        float [B]: the uniform of each row (unused, may be NULL, when greedy)
+ *   greedy   nonzero: the argmax of each row (lowest index on ties);
+ *            zero: inverse CDF of softmax(row / temperature) at u[b]
+ *   tokens   out int32 [B]
+ * It is the verification of sequences with no draft tokens.  Workspace:
+ * sv_workspace_bytes(B, 1, 0, V).
+ */
+int sv_sample(const void* logits, const float* u, int B, int V, int64_t row_stride, int dtype,
+              float temperature, int greedy, int32_t* tokens, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that suffice for any entry point at this shape (G = 1 for
+ * stochastic, ragged (k = k_max) and sampling (k = 0) calls).  Returns 0 for
+ * an invalid shape. */
 size_t sv_workspace_bytes(int B, int G, int k, int V);
 
 /* Static, human-readable text for a status code. */

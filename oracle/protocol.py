@@ -142,3 +142,90 @@ def compare_stochastic(target, draft, draft_tokens, u_accept, u_sample, *, B, k,
             rep.failures.append(f"seq {b}: tokens {tg.tolist()} vs oracle {to.tolist()} "
                                 f"(r={r_!r}, oracle cell [{cur['lo']!r}, {cur['hi']!r}))")
     return rep
+
+
+def _sample_cell(row, *, V, temperature, y, lib):
+    """Cumulative probability (before, through) token y under softmax(row/T).
+    The oracle's bonus-token distribution of a one-draft sequence whose two
+    target rows are both `row` is exactly that softmax, so its own CDF
+    routine gives the cell."""
+    t2 = np.ascontiguousarray(np.stack([row[:V], row[:V]]))
+    d1 = np.ascontiguousarray(row[None, :V])
+    return svo.emit_cdf(t2, d1, b=0, k=1, V=V, a=1, y=y, temperature=temperature, lib=lib)
+
+
+def compare_sample(logits, u, *, B, V, temperature, tokens, greedy=False, row_stride=None,
+                   lib=None) -> Report:
+    """Plain sampling, one token per row.  Greedy: identical.  Otherwise the
+    token may differ from the oracle's only where u lies within BAND of the
+    oracle's cell boundary AND within BAND of the other token's own cell."""
+    lib = lib or svo.load()
+    rs = V if row_stride is None else row_stride
+    rep = Report(n=B)
+    rows = np.ascontiguousarray(logits).reshape(B, -1)[:, :rs]
+    y_o = svo.sample(rows, u, B=B, V=V, row_stride=rs, temperature=temperature, greedy=greedy,
+                     lib=lib)
+    for b in range(B):
+        yg, yo = int(tokens[b]), int(y_o[b])
+        if yg == yo:
+            continue
+        if greedy or not (0 <= yg < V):
+            rep.failures.append(f"row {b}: token {yg} vs oracle {yo}")
+            continue
+        r_ = float(np.float32(u[b]))
+        lo_o, hi_o = _sample_cell(rows[b], V=V, temperature=temperature, y=yo, lib=lib)
+        lo_g, hi_g = _sample_cell(rows[b], V=V, temperature=temperature, y=yg, lib=lib)
+        if min(r_ - lo_o, hi_o - r_) < BAND and (lo_g - BAND) <= r_ < (hi_g + BAND):
+            rep.token_band += 1
+        else:
+            rep.failures.append(f"row {b}: token {yg} vs oracle {yo} (u={r_!r}, oracle cell "
+                                f"[{lo_o!r}, {hi_o!r}), other cell [{lo_g!r}, {hi_g!r}))")
+    return rep
+
+
+def compare_stochastic_ragged(target, draft, draft_tokens, cu, u_accept, u_sample, *, k_max, V,
+                              temperature, accept_len, tokens, px_qx=None, row_stride=None,
+                              lib=None) -> Report:
+    """Ragged batch: sequence b (k_b = cu[b+1] - cu[b] draft tokens, target
+    rows from cu[b] + b, draft rows from cu[b]) is compared as a batch of one
+    under the dense rules, or as plain sampling when k_b = 0; token slots past
+    k_b must hold -1.  px_qx: [cu[B]][2] or None."""
+    lib = lib or svo.load()
+    rs = V if row_stride is None else row_stride
+    cu = np.asarray(cu, np.int64).reshape(-1)
+    B = cu.size - 1
+    tgt = np.ascontiguousarray(target).reshape(-1, rs)
+    drf = np.ascontiguousarray(draft).reshape(-1, rs) if cu[-1] > 0 else None
+    x = np.asarray(draft_tokens, np.int32).reshape(-1)
+    ua = np.asarray(u_accept, np.float32).reshape(-1)
+    us = np.asarray(u_sample, np.float32).reshape(-1)
+    rep = Report(n=B)
+    for b in range(B):
+        d0, kb = int(cu[b]), int(cu[b + 1] - cu[b])
+        t0 = d0 + b
+        tok = np.asarray(tokens[b])
+        if np.any(tok[kb + 1:] != -1):
+            rep.failures.append(f"seq {b}: slots past k_b={kb} not -1: {tok.tolist()}")
+            continue
+        if kb == 0:
+            if int(accept_len[b]) != 0:
+                rep.failures.append(f"seq {b}: accept_len {accept_len[b]} with no drafts")
+                continue
+            r = compare_sample(tgt[t0:t0 + 1], us[b:b + 1], B=1, V=V, temperature=temperature,
+                               tokens=tok[:1], row_stride=rs, lib=lib)
+        else:
+            pq = None if px_qx is None else np.asarray(px_qx)[d0:d0 + kb][None]
+            r = compare_stochastic(tgt[t0:t0 + kb + 1], drf[d0:d0 + kb], x[None, d0:d0 + kb],
+                                   ua[None, d0:d0 + kb], us[b:b + 1], B=1, k=kb, V=V,
+                                   temperature=temperature, accept_len=accept_len[b:b + 1],
+                                   tokens=tok[None, :kb + 1], px_qx=pq, row_stride=rs, lib=lib)
+        rep.decision_band += r.decision_band
+        rep.token_band += r.token_band
+        rep.max_rel_p = max(rep.max_rel_p, r.max_rel_p)
+        rep.failures += [f"seq {b}: " + f for f in r.failures]
+    return rep
+
+
+def compare_greedy_ragged(oracle_out: dict, accept_len, tokens) -> Report:
+    """Ragged greedy: identical accept lengths and token rows."""
+    return compare_greedy(oracle_out, accept_len, tokens)

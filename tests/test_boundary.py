@@ -36,8 +36,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["sv_status_string", "sv_verify_greedy", "sv_verify_stochastic",
-                     "sv_workspace_bytes"]
+    assert names == ["sv_sample", "sv_status_string", "sv_verify_greedy",
+                     "sv_verify_greedy_ragged", "sv_verify_stochastic",
+                     "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -76,9 +77,11 @@ def test_workspace_bytes(lib):
     for args in [(192, 1, 8, 128256), (256, 1, 8, 128256), (512, 1, 3, 129280)]:
         assert f(*args) == 0
     # bad shapes
-    for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, 0, 10), (1, 1, 1, 0), (1, 1, 65, 10),
+    for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, -1, 10), (1, 1, 1, 0), (1, 1, 65, 10),
                  (1, 600, 1, 10)]:
         assert f(*args) == 0
+    # k = 0 (plain sampling) is a valid shape
+    assert f(10, 1, 0, 1000) > 0
     # row-split: at least 8 bytes per row of every sequence
     for B in (1, 50, 100, 150, 191):
         assert f(B, 1, 8, 128256) >= B * 17 * 8
@@ -120,13 +123,13 @@ def test_greedy_null(lib, field):
     assert greedy(lib, **{field: None}) == SV_ERR_NULL
 
 
-@pytest.mark.parametrize("kw", [dict(B=-1), dict(k=0), dict(k=65), dict(V=0), dict(rs=99),
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(k=-1), dict(k=65), dict(V=0), dict(rs=99),
                                 dict(V=(1 << 28) + 1, rs=(1 << 28) + 1)])
 def test_stochastic_shape(lib, kw):
     assert stoch(lib, **kw) == SV_ERR_SHAPE
 
 
-@pytest.mark.parametrize("kw", [dict(B=-3), dict(G=0), dict(k=0), dict(V=-5), dict(rs=10),
+@pytest.mark.parametrize("kw", [dict(B=-3), dict(G=0), dict(k=-2), dict(V=-5), dict(rs=10),
                                 dict(G=300, k=3), dict(G=16, k=64)])
 def test_greedy_shape(lib, kw):
     assert greedy(lib, **kw) == SV_ERR_SHAPE
@@ -169,3 +172,81 @@ def test_empty_batch_is_a_noop(lib):
     assert stoch(lib, B=0, t=None, d=None, x=None, ua=None, us=None, al=None, tok=None,
                  ws=None, wsb=0) == SV_OK
     assert greedy(lib, B=0, t=None, x=None, al=None, tok=None, ws=None, wsb=0) == SV_OK
+
+
+def ragged(lib, **kw):
+    args = dict(t=A, d=A, x=A, cu=A, total=10, ua=A, us=A, B=2, k=3, V=100, rs=100, dtype=1,
+                tau=1.0, al=A, tok=A, dbg=None, ws=WS, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_stochastic_ragged(args["t"], args["d"], args["x"], args["cu"],
+                                           args["total"], args["ua"], args["us"], args["B"],
+                                           args["k"], args["V"], args["rs"], args["dtype"],
+                                           args["tau"], args["al"], args["tok"], args["dbg"],
+                                           args["ws"], args["wsb"], args["stream"])
+
+
+def greedy_ragged(lib, **kw):
+    args = dict(t=A, x=A, cu=A, total=10, B=2, k=3, V=100, rs=100, dtype=0, al=A, tok=A,
+                ws=WS, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_greedy_ragged(args["t"], args["x"], args["cu"], args["total"],
+                                       args["B"], args["k"], args["V"], args["rs"],
+                                       args["dtype"], args["al"], args["tok"], args["ws"],
+                                       args["wsb"], args["stream"])
+
+
+def sample(lib, **kw):
+    args = dict(t=A, u=A, B=2, V=100, rs=100, dtype=1, tau=1.0, greedy=0, tok=A, ws=WS,
+                wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_sample(args["t"], args["u"], args["B"], args["V"], args["rs"], args["dtype"],
+                         args["tau"], args["greedy"], args["tok"], args["ws"], args["wsb"],
+                         args["stream"])
+
+
+@pytest.mark.parametrize("field", ["t", "d", "x", "cu", "ua", "us", "al", "tok", "ws"])
+def test_ragged_null(lib, field):
+    assert ragged(lib, **{field: None}) == SV_ERR_NULL
+
+
+def test_ragged_without_drafts_needs_no_draft_buffers(lib):
+    # total_draft == 0: draft logits, tokens and uniforms may be NULL; the
+    # workspace check (too small) is the first to fail, before any launch
+    assert ragged(lib, total=0, d=None, x=None, ua=None, wsb=8) == SV_ERR_WORKSPACE
+    assert ragged(lib, total=0, d=None, x=None, ua=None, us=None) == SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(total=-1), dict(k=65), dict(k=-1), dict(B=-1),
+                                dict(rs=50)])
+def test_ragged_shape(lib, kw):
+    assert ragged(lib, **kw) == SV_ERR_SHAPE
+
+
+def test_ragged_other_checks(lib):
+    assert ragged(lib, tau=0.0) == SV_ERR_TEMPERATURE
+    assert ragged(lib, dtype=7) == SV_ERR_DTYPE
+    assert ragged(lib, wsb=16) == SV_ERR_WORKSPACE
+    assert ragged(lib, B=0, t=None, d=None, x=None, cu=None, ua=None, us=None, al=None,
+                  tok=None, ws=None, wsb=0) == SV_OK
+
+
+@pytest.mark.parametrize("field", ["t", "cu", "x", "al", "tok", "ws"])
+def test_greedy_ragged_null(lib, field):
+    assert greedy_ragged(lib, **{field: None}) == SV_ERR_NULL
+
+
+def test_greedy_ragged_checks(lib):
+    assert greedy_ragged(lib, total=-5) == SV_ERR_SHAPE
+    assert greedy_ragged(lib, dtype=3) == SV_ERR_DTYPE
+    assert greedy_ragged(lib, wsb=0) == SV_ERR_WORKSPACE
+
+
+def test_sample_checks(lib):
+    assert sample(lib, t=None) == SV_ERR_NULL
+    assert sample(lib, u=None) == SV_ERR_NULL          # stochastic needs uniforms
+    assert sample(lib, tok=None) == SV_ERR_NULL
+    assert sample(lib, u=None, greedy=1, wsb=0) == SV_ERR_WORKSPACE  # greedy: u unused
+    assert sample(lib, tau=-1.0) == SV_ERR_TEMPERATURE
+    assert sample(lib, dtype=9) == SV_ERR_DTYPE
+    assert sample(lib, V=0) == SV_ERR_SHAPE
+    assert sample(lib, B=0, t=None, u=None, tok=None, ws=None, wsb=0) == SV_OK

@@ -306,3 +306,164 @@ def test_deterministic(index):
     for o in outs[1:]:
         for u, v in zip(outs[0], o):
             assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+# ------------------------------------------------- ragged draft lengths ------
+
+def make_ragged(seed, B, k_max, V, dtype, tau, kb=None, special=None):
+    """Packed ragged batch: k_b draft tokens for sequence b (some zero), the
+    draft row for position i near the target row for position i, draft
+    tokens sampled from the draft rows."""
+    rng = np.random.default_rng(seed)
+    if kb is None:
+        kb = rng.integers(0, k_max + 1, size=B)
+    kb = np.asarray(kb, np.int64)
+    cu = np.concatenate([[0], np.cumsum(kb)]).astype(np.int32)
+    n = int(cu[-1])
+    t64 = rng.standard_normal((n + B, V)) * 3
+    if special == "neginf":
+        t64[rng.random(t64.shape) < 0.1] = -np.inf
+        t64[:, 0] = 0.0
+    d64 = np.empty((n, V))
+    for b in range(B):
+        d0, t0 = int(cu[b]), int(cu[b]) + b
+        d64[d0:d0 + kb[b]] = t64[t0:t0 + kb[b]] + rng.standard_normal((kb[b], V)) * 0.5
+    d64[np.isnan(d64)] = -np.inf
+    t = W.round_logits(t64, dtype)
+    d = W.round_logits(d64, dtype)
+    x = W.gumbel_max(rng, W.as_f64(d, dtype), tau).astype(np.int32) if n else \
+        np.zeros(0, np.int32)
+    if special == "oov" and n:
+        x[::3] = V + 1
+    ua = W.exact_uniforms(rng, n) if n else np.zeros(0, np.float32)
+    us = W.exact_uniforms(rng, B)
+    return cu, t, d, x, ua, us
+
+
+def run_ragged(cu, t, d, x, ua, us, k_max, tau, dtype, pad=0, unaligned=False):
+    B = cu.size - 1
+    n = int(cu[-1])
+    V = t.shape[-1]
+    tt, th, rs = logits_to_device(t, dtype, pad, unaligned)
+    dt, dh, _ = logits_to_device(d if n else np.zeros((1, V), t.dtype), dtype, pad, unaligned)
+    cud, xd, uad, usd = dev(cu), dev(x), dev(ua), dev(us)
+    dbg = torch.full((n, 2), -1.0, dtype=torch.float32, device=DEV)
+    a, tok = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau,
+                                                 dbg_px_qx=dbg)
+    a2, tok2 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau)
+    ag, tokg = binding.sv_verify_greedy_ragged(tt, xd, cud, k_max)
+    torch.cuda.synchronize()
+    kw = dict(k_max=k_max, V=V, temperature=tau, row_stride=rs)
+    rep = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a.cpu().numpy(),
+                                             tokens=tok.cpu().numpy(), px_qx=dbg.cpu().numpy(),
+                                             **kw)
+    rep2 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us,
+                                              accept_len=a2.cpu().numpy(),
+                                              tokens=tok2.cpu().numpy(), **kw)
+    rep.failures += ["(no diagnostics) " + f for f in rep2.failures]
+    og = svo.verify_greedy_ragged(th, x, cu, k_max=k_max, V=V, row_stride=rs)
+    repg = protocol.compare_greedy_ragged(og, ag.cpu().numpy(), tokg.cpu().numpy())
+    rep.failures += ["(greedy) " + f for f in repg.failures]
+    return rep, a.cpu().numpy()
+
+
+RAGGED_CASES = [
+    # (B, k_max, V, dtype, tau, pad, unaligned, special)
+    (1, 1, 1, W.F32, 1.0, 0, False, None),
+    (9, 4, 7, W.BF16, 1.0, 0, False, None),
+    (37, 5, 4103, W.BF16, 0.8, 0, False, None),
+    (13, 8, 2053, W.F32, 1.0, 3, True, "oov"),
+    (8, 8, 128256, W.BF16, 1.0, 0, False, None),
+    (5, 3, 100003, W.F32, 1.2, 0, True, "neginf"),
+    # B >= 192: one workgroup per sequence
+    (200, 8, 1000, W.BF16, 1.0, 0, False, None),
+    (256, 4, 20011, W.F32, 0.7, 0, True, "neginf"),
+    (300, 2, 9, W.BF16, 1.0, 2, False, "oov"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_CASES, ids=lambda c: "B{}_k{}_V{}_{}_t{}_p{}_u{}_{}".format(
+    c[0], c[1], c[2], "bf16" if c[3] else "f32", c[4], c[5], int(c[6]), c[7]))
+def test_ragged(case):
+    B, k_max, V, dtype, tau, pad, unal, special = case
+    print(f"ragged case {case}", flush=True)
+    cu, t, d, x, ua, us = make_ragged(hash(case) & 0xFFFF, B, k_max, V, dtype, tau,
+                                      special=special)
+    rep, _ = run_ragged(cu, t, d, x, ua, us, k_max, tau, dtype, pad, unal)
+    print(rep.summary())
+    assert rep.ok(), rep.summary()
+
+
+@pytest.mark.parametrize("B", [6, 200])
+def test_ragged_no_drafts(B):
+    """Every k_b = 0: the call samples each sequence's one target row."""
+    print(f"ragged no drafts B={B}", flush=True)
+    cu, t, d, x, ua, us = make_ragged(B, B, 4, 3001, W.BF16, 1.0, kb=np.zeros(B))
+    rep, a = run_ragged(cu, t, d, x, ua, us, 4, 1.0, W.BF16)
+    assert rep.ok(), rep.summary()
+    assert np.all(a == 0)
+
+
+@pytest.mark.parametrize("B", [4, 256])
+def test_ragged_uniform_matches_dense(B):
+    """Every k_b = k: the ragged call returns exactly what the dense call does."""
+    print(f"ragged uniform B={B}", flush=True)
+    k, V = 5, 4103
+    t, d, x, ua, us = make_stochastic(B + 77, B, k, V, W.BF16, 1.0)
+    cu = (np.arange(B + 1) * k).astype(np.int32)
+    tt, _, _ = logits_to_device(t, W.BF16)
+    dt, _, _ = logits_to_device(d, W.BF16)
+    args = [dev(x.reshape(-1)), dev(cu), dev(ua.reshape(-1)), dev(us)]
+    dbg_r = torch.empty((B * k, 2), dtype=torch.float32, device=DEV)
+    dbg_d = torch.empty((B, k, 2), dtype=torch.float32, device=DEV)
+    a_r, t_r = binding.sv_verify_stochastic_ragged(tt.reshape(-1, V), dt.reshape(-1, V),
+                                                   *args, k, 1.0, dbg_px_qx=dbg_r)
+    a_d, t_d = binding.sv_verify_stochastic(tt, dt, dev(x), dev(ua), dev(us), 1.0, dbg_px_qx=dbg_d)
+    g_r, gt_r = binding.sv_verify_greedy_ragged(tt.reshape(-1, V), args[0], args[1], k)
+    g_d, gt_d, _ = binding.sv_verify_greedy(tt, dev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(a_r, a_d) and torch.equal(t_r, t_d)
+    assert torch.equal(dbg_r.view(B, k, 2), dbg_d)
+    assert torch.equal(g_r, g_d) and torch.equal(gt_r, gt_d)
+
+
+# --------------------------------------------------------- plain sampling ----
+
+SAMPLE_CASES = [
+    # (B, V, dtype, tau, pad, unaligned, special)
+    (1, 1, W.F32, 1.0, 0, False, None),
+    (7, 9, W.BF16, 0.7, 0, False, None),
+    (37, 4103, W.F32, 1.0, 2, True, "neginf"),
+    (16, 128256, W.BF16, 1.0, 0, False, None),
+    (3, 600000, W.BF16, 1.3, 0, False, None),
+    (200, 1000, W.BF16, 1.0, 0, False, "ties"),
+    (300, 32000, W.F32, 0.8, 0, True, None),
+]
+
+
+@pytest.mark.parametrize("case", SAMPLE_CASES, ids=lambda c: "B{}_V{}_{}_t{}_p{}_u{}_{}".format(
+    c[0], c[1], "bf16" if c[2] else "f32", c[3], c[4], int(c[5]), c[6]))
+def test_sample(case):
+    B, V, dtype, tau, pad, unal, special = case
+    print(f"sample case {case}", flush=True)
+    rng = np.random.default_rng(hash(case) & 0xFFFF)
+    if special == "ties":
+        t64 = rng.integers(-3, 3, size=(B, V)).astype(np.float64)
+    else:
+        t64 = rng.standard_normal((B, V)) * 3
+    if special == "neginf":
+        t64[rng.random(t64.shape) < 0.2] = -np.inf
+        t64[:, -1] = 1.0
+    t = W.round_logits(t64, dtype)
+    u = W.exact_uniforms(rng, B)
+    tt, th, rs = logits_to_device(t, dtype, pad, unal)
+    y = binding.sv_sample(tt, dev(u), tau)
+    yg = binding.sv_sample(tt, None, greedy=True)
+    torch.cuda.synchronize()
+    rep = protocol.compare_sample(th, u, B=B, V=V, temperature=tau, tokens=y.cpu().numpy(),
+                                  row_stride=rs)
+    repg = protocol.compare_sample(th, None, B=B, V=V, temperature=tau, tokens=yg.cpu().numpy(),
+                                   greedy=True, row_stride=rs)
+    print(rep.summary())
+    assert rep.ok(), rep.summary()
+    assert repg.ok(), repg.summary()
