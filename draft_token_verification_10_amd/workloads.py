@@ -19,6 +19,12 @@ noise), which draws exactly from that softmax.  Uniforms are exact float32
 values ``m * 2**-24`` with ``m`` uniform on ``[0, 2**24)``, so they lie in
 ``[0, 1)``.
 
+Two derived inputs reuse a workload's rows: a ragged batch (``ragged``), in
+which sequence b keeps only its first k_b ~ U{1..k} draft positions (drawn
+from a seventh stream), packed without gaps; and a sampling batch
+(``sample_rows``), the first target row of every sequence with its sample
+uniform.
+
 The workloads:
 
 0. ``B=1, k=4, V=32000`` fp32, tau 1: target ~ N(0, 3^2) i.i.d., draft =
@@ -49,8 +55,8 @@ import numpy as np
 F32 = 0
 BF16 = 1
 
-# stream indices
-S_TARGET, S_DRAFT, S_SPIKE, S_TOKEN, S_UACC, S_USAMP = range(6)
+# stream indices (S_LEN: per-sequence draft lengths of the ragged variant)
+S_TARGET, S_DRAFT, S_SPIKE, S_TOKEN, S_UACC, S_USAMP, S_LEN = range(7)
 
 
 @dataclass(frozen=True)
@@ -201,3 +207,60 @@ def make(index: int, seqs=None, threads: int | None = None) -> Batch:
                  draft_tokens=stack("draft_tokens"), u_accept=stack("u_accept").reshape(n, -1),
                  u_sample=stack("u_sample").reshape(n), greedy_tokens=stack("greedy_tokens"),
                  seqs=seqs)
+
+
+@dataclass
+class RaggedBatch:
+    """Packed ragged batch.  target: [n + B][V] (sequence b's k_b + 1 rows from
+    row cu[b] + b); draft: [n][V] (from row cu[b]); draft_tokens, u_accept:
+    [n]; cu: int32 [B + 1] cumulative draft lengths; u_sample: [B]."""
+    spec: Spec
+    k_max: int
+    kb: np.ndarray
+    cu: np.ndarray
+    target: np.ndarray
+    draft: np.ndarray
+    draft_tokens: np.ndarray
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+
+
+def ragged_lengths(spec: Spec, seqs=None) -> np.ndarray:
+    """k_b ~ U{1..k} per sequence, from the length stream."""
+    seqs = np.arange(spec.B) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    return np.array([int(rng_for(spec.index, S_LEN, int(b)).integers(1, spec.k + 1))
+                     for b in seqs], dtype=np.int64)
+
+
+def ragged(batch: Batch) -> RaggedBatch:
+    """Keep the first k_b draft positions of every sequence of a dense
+    single-candidate batch (target rows 0..k_b, draft rows 0..k_b-1) and pack
+    them.  Row k_b of the target is the row that follows the last kept draft
+    token, so the packed batch is a valid verification input."""
+    s = batch.spec
+    if s.G != 1 or batch.draft is None:
+        raise ValueError("ragged batches are built from single-candidate stochastic workloads")
+    kb = ragged_lengths(s, batch.seqs)
+    B = len(kb)
+    cu = np.concatenate([[0], np.cumsum(kb)]).astype(np.int32)
+    n = int(cu[-1])
+    V = s.V
+    target = np.empty((n + B, V), batch.target.dtype)
+    draft = np.empty((n, V), batch.draft.dtype)
+    x = np.empty(n, np.int32)
+    ua = np.empty(n, np.float32)
+    for b in range(B):
+        k, d0 = int(kb[b]), int(cu[b])
+        target[d0 + b:d0 + b + k + 1] = batch.target[b, :k + 1]
+        draft[d0:d0 + k] = batch.draft[b, :k]
+        x[d0:d0 + k] = batch.draft_tokens[b, :k]
+        ua[d0:d0 + k] = batch.u_accept[b, :k]
+    return RaggedBatch(spec=s, k_max=s.k, kb=kb, cu=cu, target=target, draft=draft,
+                       draft_tokens=x, u_accept=ua, u_sample=batch.u_sample.copy())
+
+
+def sample_rows(batch: Batch):
+    """One row per sequence for plain sampling: target row 0 ([B][V]) and the
+    sequence's sample uniform ([B])."""
+    t = batch.target if batch.spec.G == 1 else batch.target[:, 0]
+    return np.ascontiguousarray(t[:, 0]), batch.u_sample.copy()

@@ -1,0 +1,56 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU)."""
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from draft_token_verification_10_amd import workloads as W
+
+
+def test_algorithmic_bytes_workload2():
+    s = W.SPECS[2]
+    # the figures the benchmark is quoted on
+    assert bench.algorithmic_bytes(s, "stochastic") == 1_116_367_872
+    assert bench.algorithmic_bytes(s, "greedy") == 591_023_104
+
+
+def test_ragged_bytes_reduce_to_dense():
+    s = W.SPECS[2]
+    kb = np.full(s.B, s.k)
+    cu_bytes = 4 * (s.B + 1)
+    assert bench.algorithmic_bytes(s, "ragged", kb) == \
+        bench.algorithmic_bytes(s, "stochastic") + cu_bytes
+    # greedy: the same minus best_cand, plus cu
+    assert bench.algorithmic_bytes(s, "ragged", kb, greedy=True) == \
+        bench.algorithmic_bytes(s, "greedy") - 4 * s.B + cu_bytes
+
+
+def test_sample_bytes():
+    s = W.SPECS[2]
+    assert bench.algorithmic_bytes(s, "sample") == s.B * s.V * 2 + 8 * s.B
+    assert bench.algorithmic_bytes(s, "sample", greedy=True) == s.B * s.V * 2 + 4 * s.B
+
+
+def test_copies_defeat_last_level_cache():
+    assert bench.n_copies(1_116_367_872, None) == 1
+    assert bench.n_copies(147_750_912, None) * 147_750_912 >= bench.COLD_BYTES
+    assert bench.n_copies(10, None) == bench.MAX_COPIES
+    assert bench.n_copies(10, 3) == 3
+
+
+def test_ragged_batch_packing():
+    b = W.make(1, seqs=range(5))
+    r = W.ragged(b)
+    assert r.cu[0] == 0 and np.all(np.diff(r.cu) == r.kb) and np.all((r.kb >= 1) & (r.kb <= 4))
+    for i in range(5):
+        k, d0 = int(r.kb[i]), int(r.cu[i])
+        assert np.array_equal(r.target[d0 + i:d0 + i + k + 1], b.target[i, :k + 1])
+        assert np.array_equal(r.draft[d0:d0 + k], b.draft[i, :k])
+        assert np.array_equal(r.draft_tokens[d0:d0 + k], b.draft_tokens[i, :k])
+
+
+def test_several_gpus_refused():
+    p = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True,
+                       text=True, cwd=bench.ROOT, timeout=120)
+    assert p.returncode == 2 and "one GPU" in p.stderr
