@@ -38,16 +38,27 @@ struct Plan {
     int S;
     int slice_len;
     int SD;  // row-split stochastic: draw workgroups per sequence
+    bool slice_draw;  // plain sampling: draw from slice statistics
     bool vec;
     size_t ws_bytes;
 };
 
+// Layout choice beyond use_seq_resident():
+//   ROW_SPLIT  the caller forces the row-split layout (ragged batches of
+//              unequal lengths with diagnostics: every row is read, and one
+//              workgroup per sequence would wait on the longest sequence);
+//   SAMPLE     plain sampling: row-split with sliced rows (the draw reads one
+//              slice again instead of the whole row).
+enum PlanFlags { kPlanDefault = 0, kPlanRowSplit = 1, kPlanSample = 2 };
+
 int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dtype,
-              bool stochastic, const void* const* row_bases, int n_bases, Plan* pl) {
+              bool stochastic, int flags, const void* const* row_bases, int n_bases,
+              Plan* pl) {
     const int es = elem_size(dtype);
     bool vec = ((row_stride * es) % 16) == 0;
     for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
-    pl->seq = sv::use_seq_resident(B, G);
+    pl->seq = flags == kPlanDefault && sv::use_seq_resident(B, G);
+    pl->slice_draw = false;
     pl->rows_per_seq = rows_per_seq;
     pl->vec = vec;
     if (pl->seq) {
@@ -58,7 +69,8 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
         return B > kMaxSeqGrid ? SV_ERR_SHAPE : SV_OK;
     }
     const int E = vec ? 16 / es : 1;
-    const int S0 = sv::plan_slices((long long)B * rows_per_seq, V);
+    const int S0 = (flags & kPlanSample) ? sv::plan_slices_sample((long long)B * rows_per_seq, V)
+                                         : sv::plan_slices((long long)B * rows_per_seq, V);
     // slice length: a whole number of chunks, then drop empty slices
     const int chunks = (V + E - 1) / E;
     const int per = (chunks + S0 - 1) / S0;
@@ -67,6 +79,7 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
     pl->S = S;
     pl->slice_len = slice_len;
+    pl->slice_draw = stochastic && (flags & kPlanSample);
     pl->SD = stochastic ? sv::plan_draw_slices(B, sv::draw_tiles(V / E, V % E)) : 1;
     if ((long long)B * pl->SD > kMaxGrid) return SV_ERR_SHAPE;
     pl->ws_bytes = sv::workspace_bytes_for(B, rows_per_seq, S, stochastic);
@@ -81,12 +94,12 @@ int check_workspace(const void* ws, size_t bytes, const Plan& pl) {
     return SV_OK;
 }
 
-// Workspace bytes for one entry point at this shape (an upper bound over the
-// load paths: the slice count before rounding to whole chunks).
-size_t workspace_need(int B, int G, int rows_per_seq, int V, bool stochastic) {
-    if (sv::use_seq_resident(B, G)) return 0;
-    return sv::workspace_bytes_for(B, rows_per_seq, sv::plan_slices((long long)B * rows_per_seq, V),
-                                   stochastic);
+// Workspace bytes of the row-split layout at this shape (an upper bound over
+// the load paths: the slice count before rounding to whole chunks).
+size_t rowsplit_need(int B, int rows_per_seq, int V, bool stochastic, bool sample) {
+    const long long rows = (long long)B * rows_per_seq;
+    const int S = sample ? sv::plan_slices_sample(rows, V) : sv::plan_slices(rows, V);
+    return sv::workspace_bytes_for(B, rows_per_seq, S, stochastic);
 }
 
 }  // namespace
@@ -97,9 +110,12 @@ extern "C" {
 
 size_t sv_workspace_bytes(int B, int G, int k, int V) {
     if (check_shape(B, G, k, V, V) != SV_OK) return 0;
-    // Enough for either entry point: stochastic (one candidate) and greedy.
-    const size_t s = workspace_need(B, 1, 2 * k + 1, V, true);
-    const size_t g = workspace_need(B, G, G * (k + 1), V, false);
+    // Enough for every entry point: the stochastic ones (one candidate) may
+    // take the row-split layout at any B (sampling always does, ragged
+    // batches with diagnostics may), greedy ones only below the
+    // sequence-resident threshold.
+    const size_t s = rowsplit_need(B, 2 * k + 1, V, true, k == 0);
+    const size_t g = sv::use_seq_resident(B, G) ? 0 : rowsplit_need(B, G * (k + 1), V, false, false);
     return s > g ? s : g;
 }
 
@@ -140,8 +156,13 @@ int stochastic_impl(const void* target, const void* draft, const int32_t* x, con
     if (!target || !us || !tokens) return SV_ERR_NULL;
     if (drafts && (!draft || !x || !ua)) return SV_ERR_NULL;
     const void* bases[2] = {target, drafts ? draft : target};
+    int flags = kPlanDefault;
+    if (!cu && k == 0) flags = kPlanSample;
+    // Unequal ragged lengths (known from the total alone) with every row to
+    // be read: balance rows, not sequences, over the GPU.
+    if (cu && dbg && total_draft < (long long)B * k) flags = kPlanRowSplit;
     Plan pl;
-    st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, true, bases, 2, &pl);
+    st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, true, flags, bases, 2, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;
@@ -160,9 +181,13 @@ int stochastic_impl(const void* target, const void* draft, const int32_t* x, con
     if (!pl.seq) {
         char* w = static_cast<char*>(workspace) + sv::part_bytes(B, pl.rows_per_seq, pl.S);
         p.tilesum = reinterpret_cast<float*>(w);
-        p.meta = reinterpret_cast<int*>(w + sv::tilesum_bytes(B));
+        w += sv::tilesum_bytes(B);
+        p.meta = reinterpret_cast<int*>(w);
+        w += sv::meta_bytes(B);
+        p.xl = reinterpret_cast<float*>(w);
     }
     p.SD = pl.SD;
+    p.slice_draw = pl.slice_draw ? 1 : 0;
     p.cu = cu;
     p.total_draft = total_draft;
     p.row_stride = row_stride;
@@ -191,7 +216,7 @@ int greedy_impl(const void* target, const int32_t* x, const int32_t* cu, long lo
     if (!target || !tokens || (drafts && !x)) return SV_ERR_NULL;
     const void* bases[1] = {target};
     Plan pl;
-    st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, false, bases, 1, &pl);
+    st = make_plan(B, G, G * (k + 1), V, row_stride, dtype, false, kPlanDefault, bases, 1, &pl);
     if (st != SV_OK) return st;
     st = check_workspace(workspace, workspace_bytes, pl);
     if (st != SV_OK) return st;

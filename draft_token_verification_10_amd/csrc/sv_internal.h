@@ -43,6 +43,25 @@ inline int plan_slices(long long rows, int V) {
     return (int)s;
 }
 
+// Plain sampling (no draft positions) always takes the row-split layout with
+// rows cut into slices of at most about kSampleSliceElems logits: the
+// statistics kernel then leaves per-slice normalisers, from which the draw
+// picks the slice holding r * Z and reads only that slice again.  (The bonus
+// token of a verification could be drawn the same way, but a single group
+// re-reading a slice measured slower there than the tile sums spread over
+// SD groups.)
+constexpr int kSampleSliceElems = 16384;
+
+inline int plan_slices_sample(long long rows, int V) {
+    int s = plan_slices(rows, V);
+    long long need = (V + (long long)kSampleSliceElems - 1) / kSampleSliceElems;
+    long long cap = V / kMinSliceElems;
+    if (cap < 1) cap = 1;
+    if (need > cap) need = cap;
+    if (need > kMaxSlices) need = kMaxSlices;
+    return s > need ? s : (int)need;
+}
+
 // Inverse-CDF tiles: a row's chunks are cut into at most kMaxTiles tiles of
 // whole 256-chunk rounds, plus one tile for its trailing logits.
 constexpr int kMaxTiles = 256;
@@ -69,15 +88,18 @@ inline int plan_draw_slices(int B, int tiles) {
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S],
-// then (stochastic only) tile sums float [B][kMaxTiles + 1] and the per
-// sequence draw parameters int4 [B].
+// then (stochastic only) tile sums float [B][kMaxTiles + 1], the per
+// sequence draw parameters int4 [B] and the logit at each row's draft token
+// float [B][rows_per_seq].
 inline size_t part_bytes(int B, int rows_per_seq, int S) {
     return round256((size_t)B * rows_per_seq * S * 8);
 }
 inline size_t tilesum_bytes(int B) { return round256((size_t)B * (kMaxTiles + 1) * 4); }
+inline size_t meta_bytes(int B) { return round256((size_t)B * 16); }
+inline size_t xl_bytes(int B, int rows_per_seq) { return round256((size_t)B * rows_per_seq * 4); }
 inline size_t workspace_bytes_for(int B, int rows_per_seq, int S, bool stochastic) {
     size_t n = part_bytes(B, rows_per_seq, S);
-    if (stochastic) n += tilesum_bytes(B) + round256((size_t)B * 16);
+    if (stochastic) n += tilesum_bytes(B) + meta_bytes(B) + xl_bytes(B, rows_per_seq);
     return n;
 }
 
@@ -94,7 +116,9 @@ struct Params {
     float* part;          // row-split only: [B][rows_per_seq][S][2]
     float* tilesum;       // row-split stochastic: [B][kMaxTiles + 1]
     int* meta;            // row-split stochastic: [B][4] draw parameters
+    float* xl;            // row-split stochastic: [B][rows_per_seq] logit at the row's draft token
     int SD;               // row-split stochastic: draw workgroups per sequence
+    int slice_draw;       // row-split plain sampling (dense, k = 0): draw from slice statistics
     const int32_t* cu;    // ragged batches: cumulative draft lengths [B+1], else null
     long long total_draft;  // ragged batches: draft rows in the buffers
     long long row_stride; // elements

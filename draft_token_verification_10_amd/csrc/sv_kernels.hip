@@ -707,6 +707,12 @@ struct StochFin {
     float Z[MAX_ROWS_STOCH];
     float px[kMaxK];
     float qx[kMaxK];
+    float uv[kMaxK];  // acceptance uniforms
+    int xv[kMaxK];    // draft tokens (row-split)
+    float tl[kMaxK];  // target / draft logit at the draft token (row-split)
+    float dl[kMaxK];
+    int js;           // slice draw: the chosen slice, the uniform within it,
+    float rf, Rm;     // and the row's reference
     float tile_part[(MAX_TILES + 1) * (NT / 64)];
     float tile_excl[MAX_TILES + 1];
 };
@@ -719,6 +725,7 @@ __device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin
     const int32_t* x = p.tokens_in + s.d0;
     for (int i = tid; i < k; i += NT) {
         const int xi = x[i];
+        sm.uv[i] = p.u_accept[s.d0 + i];
         float pi = 0.0f, qi = 0.0f;
         if (xi >= 0 && xi < V) {
             const float tv = load_elem<DT>(stoch_row<DT>(p, s, i), xi);
@@ -735,10 +742,10 @@ __device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin
     }
     __syncthreads();
     if (tid == 0) {
-        const float* u = p.u_accept + s.d0;
+        // all operands in LDS: no memory round trip per position
         int a = k;
         for (int i = 0; i < k; ++i)
-            if (!(u[i] * sm.qx[i] < sm.px[i])) {
+            if (!(sm.uv[i] * sm.qx[i] < sm.px[i])) {
                 a = i;
                 break;
             }
@@ -1068,6 +1075,11 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
     const Row<DT, VEC> row(rp + (size_t)v0 * elem_bytes<DT>(), v1 - v0);
     float* dst = p.part + ((size_t)b * per_seq + item) * 2;
     if (STOCH) {
+        // The draft token of this row's position (target rows 0..k-1, draft
+        // rows k+1..2k); the slice holding it also leaves the logit there,
+        // so the finishing kernels need no gather of their own.
+        int xi = -1;
+        if (p.xl && r != sq.k) xi = p.tokens_in[sq.d0 + (r < sq.k ? r : r - sq.k - 1)];
         SoftAcc acc;
         stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
         float R, Z;
@@ -1086,6 +1098,8 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
             for (int w = 0; w < NW; ++w) ZZ += sc.g[w] * fast_exp2(sc.f[w] - RR);
             dst[0] = RR;
             dst[1] = ZZ;
+            if (xi >= v0 && xi < v1)
+                p.xl[(size_t)b * p.rows_per_seq + r] = load_elem<DT>(rp, xi);
         }
     } else {
         ArgAcc acc;
@@ -1135,6 +1149,10 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     const int k = sq.k, V = p.V, S = p.S;
     const float c = p.c;
     const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
+    const float* xl = p.xl + (size_t)b * p.rows_per_seq;
+    const int32_t* x = p.tokens_in + sq.d0;
+    // One round of independent loads: the row statistics, the draft tokens,
+    // the logits at them (left by the statistics kernel) and the uniforms.
     for (int r = tid; r < 2 * k + 1; r += NT) {
         float R = -FLT_MAX;
         for (int j = 0; j < S; ++j) R = fmaxf(R, part[(r * S + j) * 2]);
@@ -1144,16 +1162,19 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
         sm.R[r] = R;
         sm.Z[r] = Z;
     }
-    __syncthreads();
-    const int32_t* x = p.tokens_in + sq.d0;
     for (int i = tid; i < k; i += NT) {
-        const int xi = x[i];
+        sm.xv[i] = x[i];
+        sm.uv[i] = p.u_accept[sq.d0 + i];
+        sm.tl[i] = xl[i];
+        sm.dl[i] = xl[k + 1 + i];
+    }
+    __syncthreads();
+    for (int i = tid; i < k; i += NT) {
+        const int xi = sm.xv[i];
         float pi = 0.0f, qi = 0.0f;
-        if (xi >= 0 && xi < V) {
-            const float tv = load_elem<DT>(stoch_row<DT>(p, sq, i), xi);
-            const float dv = load_elem<DT>(stoch_row<DT>(p, sq, k + 1 + i), xi);
-            pi = fast_exp2(fmaf(tv, c, -sm.R[i])) / sm.Z[i];
-            qi = fast_exp2(fmaf(dv, c, -sm.R[k + 1 + i])) / sm.Z[k + 1 + i];
+        if (xi >= 0 && xi < V) {  // else nothing was left in tl/dl
+            pi = fast_exp2(fmaf(sm.tl[i], c, -sm.R[i])) / sm.Z[i];
+            qi = fast_exp2(fmaf(sm.dl[i], c, -sm.R[k + 1 + i])) / sm.Z[k + 1 + i];
         }
         sm.px[i] = pi;
         sm.qx[i] = qi;
@@ -1164,10 +1185,9 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     }
     __syncthreads();
     if (tid == 0) {
-        const float* u = p.u_accept + sq.d0;
         int a = k;
         for (int i = 0; i < k; ++i)
-            if (!(u[i] * sm.qx[i] < sm.px[i])) {
+            if (!(sm.uv[i] * sm.qx[i] < sm.px[i])) {
                 a = i;
                 break;
             }
@@ -1225,6 +1245,56 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     }
 }
 
+// Plain sampling of row r from the statistics kernel's slice normalisers:
+// the slice whose cumulative weight first exceeds u * total, then the inverse
+// CDF inside that slice at the uniform's position within the slice's weight.
+// Only the slice is read again.  All threads call.
+template <int DT, bool VEC, int NT>
+__device__ int slice_draw(const Params& p, const Seq& sq, int b, int r, float u,
+                          StochFin<NT>& sm) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int S = p.S;  // <= kMaxSlices = 64: one wave holds every slice
+    const float* ps = p.part + ((size_t)b * p.rows_per_seq + r) * S * 2;
+    if (tid < 64) {
+        const float Rj = lane < S ? ps[2 * lane] : -FLT_MAX;
+        const float Zj = lane < S ? ps[2 * lane + 1] : 0.0f;
+        const float Rm = wave_max(Rj);
+        const float Wj = lane < S ? Zj * fast_exp2(Rj - Rm) : 0.0f;
+        const float incl = wave_incl_scan(Wj);
+        const float T = u * __shfl(incl, 63);
+        const unsigned long long hit = __ballot(lane < S && Wj > 0.0f && incl > T);
+        int js;
+        float rf;
+        if (hit) {
+            js = __ffsll(hit) - 1;
+            const float w = __shfl(Wj, js);
+            rf = fmaxf(0.0f, (T - (__shfl(incl, js) - w)) / w);
+        } else {
+            // rounding left u * total at or above the last sum: the last
+            // slice with weight (whose own draw then falls back to its last
+            // positive-weight index)
+            const unsigned long long pos = __ballot(lane < S && Wj > 0.0f);
+            js = pos ? 63 - __clzll(pos) : -1;
+            rf = 1.0f;
+        }
+        if (lane == 0) {
+            sm.js = js;
+            sm.rf = rf;
+            sm.Rm = Rm;
+        }
+    }
+    __syncthreads();
+    const int js = sm.js;
+    if (js < 0) return 0;
+    const int v0 = js * p.slice_len;
+    const int v1 = min(p.V, v0 + p.slice_len);
+    const char* base = stoch_row<DT>(p, sq, r) + (size_t)v0 * elem_bytes<DT>();
+    const TargetW tw{p.c, -sm.Rm};
+    float total;
+    return v0 + inverse_cdf_row<DT, VEC, false, NT>(base, nullptr, v1 - v0, tw, sm.rf, &total,
+                                                   sm.tile_part, sm.tile_excl, sm.sc);
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     constexpr int NT = NT_DRAW;
@@ -1235,6 +1305,7 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     const Seq sq = seq_of(p, b);
     const int k = sq.k, V = p.V;
     const float c = p.c;
+    const float rr = p.u_sample[b];
     const int* m = p.meta + (size_t)b * 4;
     const int a = m[0];
     const float w0 = __int_as_float(m[1]), w1 = __int_as_float(m[2]), w2 = __int_as_float(m[3]);
@@ -1245,7 +1316,6 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     for (int t = threadIdx.x; t < g.nt_all * NW; t += NT)
         sm.tile_part[t] = (t % NW) == 0 ? ts[t / NW] : 0.0f;
     __syncthreads();
-    const float rr = p.u_sample[b];
     float total = 0.0f;
     int y;
     if (a < k) {
@@ -1264,6 +1334,22 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
                                            sm.sc);
     }
     if (threadIdx.x == 0) p.tokens_out[(size_t)b * (p.k + 1) + a] = y;
+}
+
+// Plain sampling after the statistics kernel (no decisions to take): one
+// workgroup per row draws from its slice statistics.
+constexpr int NT_SAMPLE = 512;
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_SAMPLE) void k_sample_draw(Params p) {
+    __shared__ StochFin<NT_SAMPLE> sm;
+    const int b = blockIdx.x;
+    const Seq sq = seq_of(p, b);
+    const int y = slice_draw<DT, VEC, NT_SAMPLE>(p, sq, b, 0, p.u_sample[b], sm);
+    if (threadIdx.x == 0) {
+        p.tokens_out[b] = y;
+        if (p.accept_len) p.accept_len[b] = 0;
+    }
 }
 
 __global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
@@ -1305,6 +1391,7 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     const long long items = (long long)p.B * p.rows_per_seq * p.S;
     int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
     if (e) return e;
+    if (p.slice_draw) return launch1(k_sample_draw<DT, VEC>, p, p.B, NT_SAMPLE, stream);
     e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
     if (e) return e;
     return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);

@@ -59,11 +59,13 @@
  * page, section "Inferencia so špekulatívnym dekódovaním": the accepted
  * length decides the next step's shape).
  *
- * Workspace.  sv_workspace_bytes() gives the scratch size for a shape: 0 when
- * the batch fills the GPU on its own (one candidate and B >= 192: every
- * sequence is then verified by a single workgroup that needs no scratch),
- * otherwise room for 8 bytes of statistics per row slice.  Pass at least that
- * many bytes, 256-byte aligned (NULL is accepted when the size is 0).  Its
+ * Workspace.  sv_workspace_bytes() gives a scratch size that suffices for
+ * every entry point at a shape: room for 8 bytes of statistics per row slice
+ * plus a few bytes per row and per sequence.  Pass at least that many bytes,
+ * 256-byte aligned.  Dense verification calls with k >= 1 need none when the
+ * batch fills the GPU on its own (one candidate and B >= 192: every sequence
+ * is then verified by a single workgroup), and accept NULL with size 0 there;
+ * stochastic sampling calls (k = 0) always need it.  Its
  * contents on entry do not matter and are unspecified on return.  Two calls
  * that overlap in time on the same workspace race.
  *
