@@ -386,6 +386,89 @@ int svo_sample(const void* logits, const float* u, int B, int V,
     return bad ? -1 : 0;
 }
 
+/* Greedy tree verification: per node, in index order (a parent always
+ * precedes its children), accepted = parent accepted and token == argmax of
+ * the parent's row; then the deepest accepted node, lowest index on ties,
+ * and the walk back to the root. */
+int svo_verify_greedy_tree(const void* target, const int32_t* node_tokens,
+                           const int32_t* parents, int B, int N, int V,
+                           int64_t row_stride, int dtype, int32_t* accept_len,
+                           int32_t* tokens, int32_t* path) {
+    if (!target || !node_tokens || !parents || !accept_len || !tokens || !path) return -1;
+    if (B < 0 || N < 1 || V < 1 || row_stride < V) return -1;
+    if (dtype != SVO_F32 && dtype != SVO_BF16) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parents + (int64_t)b * N;
+        if (par[0] != -1) return -1;
+        for (int j = 1; j < N; ++j)
+            if (par[j] < 0 || par[j] >= j) return -1;
+    }
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parents + (int64_t)b * N;
+        const int32_t* tok = node_tokens + (int64_t)b * N;
+        int* acc = (int*)malloc(sizeof(int) * (size_t)N);
+        int* depth = (int*)malloc(sizeof(int) * (size_t)N);
+        if (!acc || !depth) {
+#pragma omp atomic write
+            bad = 1;
+            free(acc);
+            free(depth);
+            continue;
+        }
+        acc[0] = 1;
+        depth[0] = 0;
+        int best = 0;
+        for (int j = 1; j < N; ++j) {
+            const int pj = par[j];
+            depth[j] = depth[pj] + 1;
+            acc[j] = 0;
+            if (acc[pj]) {
+                const int g = argmax_row(target, dtype, ((int64_t)b * N + pj) * row_stride, V);
+                acc[j] = tok[j] == g;
+            }
+            if (acc[j] && depth[j] > depth[best]) best = j;
+        }
+        const int d = depth[best];
+        int32_t* out_t = tokens + (int64_t)b * N;
+        int32_t* out_p = path + (int64_t)b * N;
+        for (int i = 0; i < N; ++i) {
+            out_t[i] = -1;
+            out_p[i] = -1;
+        }
+        for (int j = best, i = d; i >= 0; j = par[j], --i) out_p[i] = j;
+        for (int i = 0; i < d; ++i) out_t[i] = tok[out_p[i + 1]];
+        out_t[d] = argmax_row(target, dtype, ((int64_t)b * N + best) * row_stride, V);
+        accept_len[b] = d;
+        free(acc);
+        free(depth);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Commit of a verified step: append the emitted tokens, advance the length,
+ * hand the last emitted token to the next step. */
+int svo_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
+               int32_t* seq_len, int32_t* history, int64_t history_stride,
+               int capacity, int32_t* next_token, int64_t next_stride) {
+    if (!accept_len || !tokens || !seq_len || !history || !next_token) return -1;
+    if (B < 0 || W < 1 || capacity < 0 || history_stride < capacity || next_stride < 1)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (accept_len[b] < 0 || accept_len[b] >= W || seq_len[b] < 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        const int a = accept_len[b];
+        const int32_t* t = tokens + (int64_t)b * W;
+        int32_t* h = history + (int64_t)b * history_stride;
+        int L = seq_len[b];
+        for (int j = 0; j <= a && L < capacity; ++j) h[L++] = t[j];
+        seq_len[b] = L;
+        next_token[(int64_t)b * next_stride] = t[a];
+    }
+    return 0;
+}
+
 int svo_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

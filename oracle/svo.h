@@ -118,6 +118,39 @@ int svo_sample(const void* logits, const float* u, int B, int V,
                int64_t row_stride, int dtype, double temperature, int greedy,
                int32_t* tokens);
 
+/* Greedy verification of a draft tree per sequence (the Top-K tree of the
+ * EAGLE scheme: Perplexity, "Accelerating Sonar through speculation", section
+ * "EAGLE").  Sequence b has N nodes; node 0 is the root (the last committed
+ * token, never verified), node j >= 1 carries draft token node_tokens[b][j]
+ * and parent parents[b][j] in [0, j) (parents[b][0] = -1).  Target row j of
+ * sequence b, at (b*N + j) * row_stride, is the target's output at node j (it
+ * predicts the token that follows node j's path).  Node j >= 1 is accepted
+ * when its parent is accepted and its token equals the argmax (lowest index)
+ * of its parent's row; the root is accepted.  The deepest accepted node wins,
+ * lowest node index among equal depths.  Outputs, each [B][N] with -1 after
+ * the used entries: tokens = the draft tokens along the root-to-winner path,
+ * then the argmax of the winner's row (so d accepted drafts give d + 1
+ * tokens); path = the node indices root, ..., winner.  accept_len [B] = the
+ * winner's depth.  Returns -1 on a bad argument or a malformed tree. */
+int svo_verify_greedy_tree(const void* target, const int32_t* node_tokens,
+                           const int32_t* parents, int B, int N, int V,
+                           int64_t row_stride, int dtype, int32_t* accept_len,
+                           int32_t* tokens, int32_t* path);
+
+/* Commit of a verified step (Perplexity, same page, sections "MTP" and
+ * "Plánovanie MTP pre Jediný Token": the accepted tokens are put in place for
+ * the next step on the GPU, without waiting for the host).  For sequence b,
+ * with a = accept_len[b] and L = seq_len[b]: the a + 1 emitted tokens
+ * tokens[b][0..a] (row width W) are appended to history[b] (row stride
+ * history_stride) at positions L, L+1, ... as far as position capacity - 1,
+ * seq_len[b] becomes min(L + a + 1, capacity) (unchanged when L >= capacity),
+ * and next_token[b * next_stride] receives tokens[b][a], the token the next
+ * step starts from.  Returns -1 on a bad argument or an accept_len outside
+ * [0, W - 1]. */
+int svo_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
+               int32_t* seq_len, int32_t* history, int64_t history_stride,
+               int capacity, int32_t* next_token, int64_t next_stride);
+
 /* Number of OpenMP threads the batched entry points use. */
 int svo_num_threads(void);
 

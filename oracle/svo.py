@@ -55,6 +55,10 @@ def _bind(lib):
     lib.svo_verify_greedy_ragged.restype = I
     lib.svo_sample.argtypes = [P, P, I, I, ctypes.c_int64, I, ctypes.c_double, I, P]
     lib.svo_sample.restype = I
+    lib.svo_verify_greedy_tree.argtypes = [P, P, P, I, I, I, ctypes.c_int64, I, P, P, P]
+    lib.svo_verify_greedy_tree.restype = I
+    lib.svo_commit.argtypes = [P, P, I, I, P, P, ctypes.c_int64, I, P, ctypes.c_int64]
+    lib.svo_commit.restype = I
     lib.svo_num_threads.argtypes = []
     lib.svo_num_threads.restype = I
     return lib
@@ -220,6 +224,48 @@ def sample(logits, u, *, B, V, row_stride=None, temperature=1.0, greedy=False, l
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out
+
+
+def verify_greedy_tree(target, node_tokens, parents, *, B, N, V, row_stride=None, lib=None):
+    """Greedy tree verification (see svo.h).  Returns accept_len [B], tokens
+    [B][N], path [B][N]."""
+    lib = lib or load()
+    target = np.ascontiguousarray(target)
+    dt = _dtype_code(target)
+    row_stride = V if row_stride is None else int(row_stride)
+    assert target.size >= B * N * row_stride
+    x = _c(node_tokens, np.int32).reshape(-1)
+    par = _c(parents, np.int32).reshape(-1)
+    assert x.size == B * N and par.size == B * N
+    out = dict(accept_len=np.zeros(B, np.int32), tokens=np.zeros((B, N), np.int32),
+               path=np.zeros((B, N), np.int32))
+    rc = lib.svo_verify_greedy_tree(_ptr(target), _ptr(x), _ptr(par), B, N, V, row_stride, dt,
+                                    _ptr(out["accept_len"]), _ptr(out["tokens"]),
+                                    _ptr(out["path"]))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def commit(accept_len, tokens, seq_len, history, *, capacity=None, next_stride=1, lib=None):
+    """Commit of a verified step (see svo.h).  seq_len [B] and history
+    [B][stride] are updated in place copies; returns (seq_len, history,
+    next_token [B * next_stride] with the tokens at multiples of next_stride)."""
+    lib = lib or load()
+    a = _c(accept_len, np.int32).reshape(-1)
+    B = a.size
+    t = _c(tokens, np.int32).reshape(B, -1)
+    W = t.shape[1]
+    sl = np.array(seq_len, dtype=np.int32).reshape(-1).copy()
+    h = np.array(history, dtype=np.int32).reshape(B, -1).copy()
+    stride = h.shape[1]
+    capacity = stride if capacity is None else int(capacity)
+    nxt = np.full(max(B * next_stride, 1), -7, np.int32)
+    rc = lib.svo_commit(_ptr(a), _ptr(t), B, W, _ptr(sl), _ptr(h), stride, capacity, _ptr(nxt),
+                        next_stride)
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return sl, h, nxt
 
 
 def num_threads(lib=None) -> int:

@@ -480,6 +480,215 @@ def pin_sample_library(lib):
         assert np.array_equal(yg, np.argmax(ti, axis=1))
 
 
+# ------------------------------------------------------------ draft trees ---
+
+def random_tree(rng, N, max_children=3):
+    """Parents of a random tree on N nodes in index order (parent < child),
+    at most max_children children per node."""
+    par = np.full(N, -1, np.int32)
+    nch = np.zeros(N, np.int64)
+    for j in range(1, N):
+        while True:
+            p = int(rng.integers(0, j))
+            if nch[p] < max_children:
+                break
+        par[j] = p
+        nch[p] += 1
+    return par
+
+
+def tree_batch(rng, B, N, V, ties=True, follow=0.6):
+    """Random trees whose node tokens often equal the parent row's argmax,
+    so that accepted paths of every depth occur."""
+    if ties:
+        t = rng.integers(-3, 3, size=(B, N, V)).astype(np.float32)
+    else:
+        t = (rng.standard_normal((B, N, V)) * 2).astype(np.float32)
+    par = np.stack([random_tree(rng, N) for _ in range(B)])
+    g = np.argmax(t, axis=-1)  # first maximum
+    x = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    for b in range(B):
+        for j in range(1, N):
+            if rng.random() < follow:
+                x[b, j] = g[b, par[b, j]]
+    x[:, 0] = -1
+    return t, x, par
+
+
+def pin_tree_bruteforce(lib):
+    """Greedy tree verification against an enumeration of every root-to-node
+    path: a path's accepted length is the number of leading edges whose child
+    token is the numpy argmax of the parent's row; the answer is the deepest
+    fully accepted path, lowest end node among equal depths."""
+    rng = np.random.default_rng(31)
+    for (B, N, V, ties) in [(40, 1, 5, True), (60, 7, 4, True), (40, 13, 6, True),
+                            (20, 20, 50, False)]:
+        t, x, par = tree_batch(rng, B, N, V, ties)
+        o = svo.verify_greedy_tree(t, x, par, B=B, N=N, V=V, lib=lib)
+        g = np.argmax(t, axis=-1)
+        for b in range(B):
+            best, best_d, best_path = 0, 0, [0]
+            for j in range(N):
+                path = [j]
+                while path[-1] != 0:
+                    path.append(int(par[b, path[-1]]))
+                path = path[::-1]
+                ok = all(x[b, path[i + 1]] == g[b, path[i]] for i in range(len(path) - 1))
+                d = len(path) - 1
+                if ok and d > best_d:
+                    best, best_d, best_path = j, d, path
+            assert o["accept_len"][b] == best_d, (b, o["accept_len"][b], best_d)
+            exp_tok = [int(x[b, n]) for n in best_path[1:]] + [int(g[b, best])]
+            assert list(o["tokens"][b, :best_d + 1]) == exp_tok
+            assert list(o["path"][b, :best_d + 1]) == best_path
+            assert np.all(o["tokens"][b, best_d + 1:] == -1)
+            assert np.all(o["path"][b, best_d + 1:] == -1)
+
+
+def pin_tree_reduces_to_linear_and_candidates(lib):
+    """A chain tree is linear greedy verification with k = N - 1; G chains of
+    length k hanging from the root are G-candidate verification when every
+    candidate's first row is the root's row."""
+    rng = np.random.default_rng(32)
+    B, k, V = 50, 5, 6
+    t = rng.integers(-2, 2, size=(B, k + 1, V)).astype(np.float32)
+    g = np.argmax(t, axis=-1)
+    xl = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    for b in range(B):
+        j = int(rng.integers(0, k + 1))
+        xl[b, :j] = g[b, :j]
+    lin = svo.verify_greedy(t, xl, B=B, k=k, V=V, lib=lib)
+    par = np.tile(np.arange(-1, k, dtype=np.int32), (B, 1))
+    xt = np.concatenate([np.full((B, 1), -1, np.int32), xl], axis=1)
+    tr = svo.verify_greedy_tree(t, xt, par, B=B, N=k + 1, V=V, lib=lib)
+    assert np.array_equal(tr["accept_len"], lin["accept_len"])
+    assert np.array_equal(tr["tokens"], lin["tokens"])
+    for b in range(B):
+        a = int(lin["accept_len"][b])
+        assert list(tr["path"][b, :a + 1]) == list(range(a + 1))
+    # G candidates sharing the root row
+    G = 4
+    tc = rng.integers(-2, 2, size=(B, G, k + 1, V)).astype(np.float32)
+    tc[:, :, 0] = tc[:, :1, 0]
+    gc = np.argmax(tc, axis=-1)
+    xc = rng.integers(0, V, size=(B, G, k)).astype(np.int32)
+    for b in range(B):
+        for c in range(G):
+            j = int(rng.integers(0, k + 1))
+            xc[b, c, :j] = gc[b, c, :j]
+    mc = svo.verify_greedy(tc, xc, B=B, G=G, k=k, V=V, lib=lib)
+    N = 1 + G * k
+    tt = np.empty((B, N, V), np.float32)
+    xt = np.full((B, N), -1, np.int32)
+    par = np.full((B, N), -1, np.int32)
+    tt[:, 0] = tc[:, 0, 0]
+    for c in range(G):
+        for i in range(k):
+            n = 1 + c * k + i
+            par[:, n] = 0 if i == 0 else n - 1
+            xt[:, n] = xc[:, c, i]
+            tt[:, n] = tc[:, c, i + 1]
+    tr = svo.verify_greedy_tree(tt, xt, par, B=B, N=N, V=V, lib=lib)
+    assert np.array_equal(tr["accept_len"], mc["accept_len"])
+    assert np.array_equal(tr["tokens"][:, :k + 1], mc["tokens"])
+    for b in range(B):
+        a = int(mc["accept_len"][b])
+        if a > 0:
+            assert tr["path"][b, 1] == 1 + int(mc["best_cand"][b]) * k
+
+
+# ----------------------------------------------------------------- commit ----
+
+def _greedy_decode(T, s0, n):
+    out = [int(s0)]
+    while len(out) < n:
+        out.append(int(np.argmax(T[out[-1]])))
+    return out
+
+
+def pin_commit_lossless_decode(lib):
+    """Speculative greedy decoding of a bigram model (the logit row for input
+    token y is T[y]), with drafts from a noisy copy D of the table, verified
+    and committed step after step -- the next step starting from the committed
+    next_token -- writes exactly the plain greedy decode of T.  Done with
+    linear drafts and with draft trees (top-2 at the root, then chains)."""
+    rng = np.random.default_rng(33)
+    V, B, n, k = 40, 12, 30, 4
+    T = (rng.standard_normal((V, V)) * 2).astype(np.float32)
+    D = (T + rng.standard_normal((V, V)) * 0.7).astype(np.float32)
+    s0 = rng.integers(0, V, size=B)
+    ref = [_greedy_decode(T, s0[b], n) for b in range(B)]
+    for mode in ("linear", "tree"):
+        cap = n + 2 * k + 2
+        hist = np.full((B, cap), -5, np.int32)
+        hist[:, 0] = s0
+        sl = np.ones(B, np.int32)
+        nxt = s0.astype(np.int32)
+        steps = 0
+        while sl.min() < n:
+            steps += 1
+            assert steps <= n
+            if mode == "linear":
+                x = np.zeros((B, k), np.int32)
+                rows = np.zeros((B, k + 1, V), np.float32)
+                for b in range(B):
+                    y = int(nxt[b])
+                    rows[b, 0] = T[y]
+                    for i in range(k):
+                        y = int(np.argmax(D[y]))
+                        x[b, i] = y
+                        rows[b, i + 1] = T[y]
+                o = svo.verify_greedy(rows, x, B=B, k=k, V=V, lib=lib)
+                W = k + 1
+            else:
+                N = 1 + 2 * 2
+                par = np.tile(np.array([-1, 0, 1, 0, 3], np.int32), (B, 1))
+                xt = np.full((B, N), -1, np.int32)
+                rows = np.zeros((B, N, V), np.float32)
+                for b in range(B):
+                    y = int(nxt[b])
+                    rows[b, 0] = T[y]
+                    top2 = np.argsort(-D[y], kind="stable")[:2]
+                    for c, first in enumerate(top2):
+                        n1, n2 = 1 + 2 * c, 2 + 2 * c
+                        xt[b, n1] = first
+                        xt[b, n2] = int(np.argmax(D[first]))
+                        rows[b, n1] = T[xt[b, n1]]
+                        rows[b, n2] = T[xt[b, n2]]
+                o = svo.verify_greedy_tree(rows, xt, par, B=B, N=N, V=V, lib=lib)
+                W = N
+            sl, hist, nx = svo.commit(o["accept_len"], o["tokens"][:, :W], sl, hist, lib=lib)
+            nxt = nx[:B]
+        for b in range(B):
+            assert list(hist[b, :n]) == ref[b], (mode, b)
+            assert int(sl[b]) <= cap and np.all(hist[b, sl[b]:] == -5)
+
+
+def pin_commit_rules(lib):
+    """Commit by hand on small cases: appended tokens, the capacity clamp, the
+    strided next-token slot, untouched history outside the appended range."""
+    acc = np.array([0, 2, 3, 1], np.int32)
+    tok = np.array([[7, -1, -1, -1], [4, 5, 6, -1], [1, 2, 3, 9], [8, 0, -1, -1]], np.int32)
+    hist = np.full((4, 6), -9, np.int32)
+    hist[:, 0] = 100 + np.arange(4)
+    sl0 = np.array([1, 4, 6, 5], np.int32)  # seq 2 full, seq 3 one slot left
+    sl, h, nx = svo.commit(acc, tok, sl0, hist, next_stride=3, lib=lib)
+    assert list(sl) == [2, 6, 6, 6]
+    assert list(h[0]) == [100, 7, -9, -9, -9, -9]
+    assert list(h[1]) == [101, -9, -9, -9, 4, 5]
+    assert list(h[2]) == [102, -9, -9, -9, -9, -9]
+    assert list(h[3]) == [103, -9, -9, -9, -9, 8]
+    assert list(nx[::3]) == [7, 6, 9, 0]
+    assert np.all(np.delete(nx, np.arange(0, 12, 3)) == -7)
+    # a capacity below the stride: slots at and past it are never written
+    sl, h, _ = svo.commit(np.array([3], np.int32), np.array([[1, 2, 3, 4]], np.int32),
+                          np.array([2], np.int32), np.full((1, 8), -9, np.int32), capacity=4,
+                          lib=lib)
+    assert list(sl) == [4] and list(h[0]) == [-9, -9, 1, 2, -9, -9, -9, -9]
+
+
 ALL_PINS = [pin_enumeration, pin_softmax, pin_bonus_searchsorted, pin_onehot_residual,
             pin_greedy_argmax, pin_greedy_bf16_ties, pin_closed_forms, pin_invariants,
-            pin_ragged_equals_dense, pin_sample_library]
+            pin_ragged_equals_dense, pin_sample_library, pin_tree_bruteforce,
+            pin_tree_reduces_to_linear_and_candidates, pin_commit_lossless_decode,
+            pin_commit_rules]

@@ -47,6 +47,21 @@ MUTANTS = [
      "return ((int64_t)b * k + i) * stride;"),
     ("softmax_no_max_shift", "prob[v] = exp((logit(base, dtype, row_off + v) - M) / tau);",
      "prob[v] = exp(logit(base, dtype, row_off + v) / tau) + 0.0 * M;"),
+    ("tree_ignores_parent_acceptance", "            if (acc[pj]) {", "            if (1) {"),
+    ("tree_argmax_of_own_row",
+     "const int g = argmax_row(target, dtype, ((int64_t)b * N + pj) * row_stride, V);",
+     "const int g = argmax_row(target, dtype, ((int64_t)b * N + j) * row_stride, V);"),
+    ("tree_last_tie", "if (acc[j] && depth[j] > depth[best]) best = j;",
+     "if (acc[j] && depth[j] >= depth[best]) best = j;"),
+    ("tree_bonus_from_parent",
+     "out_t[d] = argmax_row(target, dtype, ((int64_t)b * N + best) * row_stride, V);",
+     "out_t[d] = argmax_row(target, dtype, ((int64_t)b * N + (best ? par[best] : 0)) * row_stride, V);"),
+    ("commit_drops_extra_token", "for (int j = 0; j <= a && L < capacity; ++j) h[L++] = t[j];",
+     "for (int j = 0; j < a && L < capacity; ++j) h[L++] = t[j];"),
+    ("commit_next_is_last_draft", "next_token[(int64_t)b * next_stride] = t[a];",
+     "next_token[(int64_t)b * next_stride] = t[a > 0 ? a - 1 : 0];"),
+    ("commit_ignores_capacity", "for (int j = 0; j <= a && L < capacity; ++j) h[L++] = t[j];",
+     "for (int j = 0; j <= a && L < history_stride; ++j) h[L++] = t[j];"),
 ]
 
 
