@@ -47,6 +47,10 @@ def load(path: str | None = None):
     lib.sv_verify_greedy_ragged.restype = I
     lib.sv_sample.argtypes = [P, P, I, I, I64, I, ctypes.c_float, I, P, P, SZ, P]
     lib.sv_sample.restype = I
+    lib.sv_verify_greedy_tree.argtypes = [P, P, P, I, I, I, I64, I, P, P, P, P, SZ, P]
+    lib.sv_verify_greedy_tree.restype = I
+    lib.sv_commit.argtypes = [P, P, I, I, P, P, I64, I, P, I64, P]
+    lib.sv_commit.restype = I
     lib.sv_workspace_bytes.argtypes = [I, I, I, I]
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_status_string.argtypes = [I]
@@ -331,3 +335,74 @@ def sv_sample(logits: torch.Tensor, u: torch.Tensor | None, temperature: float =
     if st != SV_OK:
         raise SpecVerifyError(st)
     return tokens
+
+
+def sv_verify_greedy_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
+                          parents: torch.Tensor, *, accept_len=None, tokens=None, path=None,
+                          workspace=None, stream=None):
+    """Greedy verification of one draft tree per sequence.  target_logits
+    [B][N][V] (row j: the target's output at node j), node_tokens and parents
+    int32 [B][N].  Returns (accept_len [B], tokens [B][N], path [B][N])."""
+    _dev(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B][N][V]")
+    B, N, V = target_logits.shape
+    rs = _row_stride(target_logits)
+    _check_i32(node_tokens, (B, N), "node_tokens")
+    _check_i32(parents, (B, N), "parents")
+    dev = target_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, N), "tokens")
+    _check_i32(path, (B, N), "path")
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    need = sv_workspace_bytes(B, N, 0, V) if B > 0 else 0
+    if workspace is None:
+        workspace = workspace_for(need, dev, s)
+    st = load().sv_verify_greedy_tree(
+        _ptr(target_logits), _ptr(node_tokens), _ptr(parents), B, N, V, rs,
+        _dtype_code(target_logits), _ptr(accept_len), _ptr(tokens), _ptr(path), _ptr(workspace),
+        _ws_bytes(workspace), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens, path
+
+
+def sv_commit(accept_len: torch.Tensor, tokens: torch.Tensor, seq_len: torch.Tensor,
+              history: torch.Tensor, next_token: torch.Tensor, *, capacity: int | None = None,
+              stream=None):
+    """Commit a verified step on the GPU: append each sequence's emitted tokens
+    to history [B][>= capacity] (int32, rows contiguous), advance seq_len [B]
+    and write the last emitted token to next_token (a [B] int32 view whose
+    elements may be strided, e.g. column 0 of the next step's input ids)."""
+    _check_i32(accept_len, (accept_len.numel(),), "accept_len")
+    B = accept_len.numel()
+    if tokens.dim() != 2 or tokens.shape[0] != B:
+        raise ValueError("tokens must be [B][W]")
+    _check_i32(tokens, tuple(tokens.shape), "tokens")
+    _check_i32(seq_len, (B,), "seq_len")
+    _dev(history)
+    if history.dtype != torch.int32 or history.dim() != 2 or history.shape[0] != B or \
+            history.stride(1) != 1:
+        raise ValueError("history must be an int32 [B][capacity] tensor with contiguous rows")
+    _dev(next_token)
+    if next_token.dtype != torch.int32 or next_token.dim() != 1 or next_token.numel() != B:
+        raise ValueError("next_token must be an int32 [B] tensor")
+    cap = history.shape[1] if capacity is None else int(capacity)
+    if cap > history.shape[1]:
+        raise ValueError("capacity exceeds the history rows")
+    hs = history.stride(0) if B > 1 else history.shape[1]
+    ns = next_token.stride(0) if B > 1 else 1
+    dev = accept_len.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream
+    st = load().sv_commit(_ptr(accept_len), _ptr(tokens), B, tokens.shape[1], _ptr(seq_len),
+                          _ptr(history), hs, cap, _ptr(next_token), max(ns, 1),
+                          ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return seq_len, history, next_token

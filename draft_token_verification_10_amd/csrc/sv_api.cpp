@@ -77,6 +77,7 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     const int slice_len = per * E;
     const int S = (V + slice_len - 1) / slice_len;
     if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
+    if (B > kMaxSeqGrid) return SV_ERR_SHAPE;  // finishing kernels: one 1024-thread group per sequence
     pl->S = S;
     pl->slice_len = slice_len;
     pl->slice_draw = stochastic && (flags & kPlanSample);
@@ -110,12 +111,12 @@ extern "C" {
 
 size_t sv_workspace_bytes(int B, int G, int k, int V) {
     if (check_shape(B, G, k, V, V) != SV_OK) return 0;
-    // Enough for every entry point: the stochastic ones (one candidate) may
-    // take the row-split layout at any B (sampling always does, ragged
-    // batches with diagnostics may), greedy ones only below the
-    // sequence-resident threshold.
+    // Enough for every entry point at any B: the stochastic ones (one
+    // candidate) may take the row-split layout (sampling always does, ragged
+    // batches with diagnostics may), and so do greedy calls below the
+    // sequence-resident threshold and tree verification (G = N nodes, k = 0).
     const size_t s = rowsplit_need(B, 2 * k + 1, V, true, k == 0);
-    const size_t g = sv::use_seq_resident(B, G) ? 0 : rowsplit_need(B, G * (k + 1), V, false, false);
+    const size_t g = rowsplit_need(B, G * (k + 1), V, false, false);
     return s > g ? s : g;
 }
 
@@ -243,9 +244,68 @@ int greedy_impl(const void* target, const int32_t* x, const int32_t* cu, long lo
     return sv::launch_greedy(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
 }
 
+// Greedy draft-tree verification: row statistics (argmax) over all N rows of
+// every sequence, then the tree decision per sequence.
+int tree_impl(const void* target, const int32_t* node_tokens, const int32_t* parents, int B,
+              int N, int V, int64_t row_stride, int dtype, int32_t* accept_len, int32_t* tokens,
+              int32_t* path, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || N < 1 || N > SV_MAX_ROWS_PER_SEQ || V < 1 || V > kMaxV || row_stride < V)
+        return SV_ERR_SHAPE;
+    if (dtype != SV_DTYPE_F32 && dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+    if (B == 0) return SV_OK;
+    if (!target || !node_tokens || !parents || !accept_len || !tokens || !path)
+        return SV_ERR_NULL;
+    const void* bases[1] = {target};
+    Plan pl;
+    int st = make_plan(B, 1, N, V, row_stride, dtype, false, kPlanRowSplit, bases, 1, &pl);
+    if (st != SV_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, pl);
+    if (st != SV_OK) return st;
+
+    sv::Params p = {};
+    p.target = target;
+    p.tokens_in = node_tokens;
+    p.parents = parents;
+    p.path = path;
+    p.accept_len = accept_len;
+    p.tokens_out = tokens;
+    p.part = static_cast<float*>(workspace);
+    p.row_stride = row_stride;
+    p.B = B;
+    p.G = 1;
+    p.k = N - 1;  // rows b*N .. b*N + N - 1, as a dense sequence of N rows
+    p.V = V;
+    p.rows_per_seq = N;
+    p.S = pl.S;
+    p.slice_len = pl.slice_len;
+    return sv::launch_tree(p, dtype, pl.vec, stream) == 0 ? SV_OK : SV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int sv_verify_greedy_tree(const void* target_logits, const int32_t* node_tokens,
+                          const int32_t* parents, int B, int N, int V, int64_t row_stride,
+                          int dtype, int32_t* accept_len, int32_t* tokens, int32_t* path,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return tree_impl(target_logits, node_tokens, parents, B, N, V, row_stride, dtype, accept_len,
+                     tokens, path, workspace, workspace_bytes, stream);
+}
+
+int sv_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W, int32_t* seq_len,
+              int32_t* history, int64_t history_stride, int capacity, int32_t* next_token,
+              int64_t next_stride, void* stream) {
+    if (B < 0 || W < 1 || capacity < 0 || history_stride < capacity || next_stride < 1)
+        return SV_ERR_SHAPE;
+    if (B > kMaxGrid) return SV_ERR_SHAPE;
+    if (B == 0) return SV_OK;
+    if (!accept_len || !tokens || !seq_len || !history || !next_token) return SV_ERR_NULL;
+    return sv::launch_commit(accept_len, tokens, B, W, seq_len, history, history_stride, capacity,
+                             next_token, next_stride, stream) == 0
+               ? SV_OK
+               : SV_ERR_HIP;
+}
 
 int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept,

@@ -119,6 +119,8 @@ struct Params {
     float* xl;            // row-split stochastic: [B][rows_per_seq] logit at the row's draft token
     int SD;               // row-split stochastic: draw workgroups per sequence
     int slice_draw;       // row-split plain sampling (dense, k = 0): draw from slice statistics
+    const int32_t* parents;  // draft trees: parent of every node [B][N], else null
+    int32_t* path;        // draft trees: node indices root .. winner [B][N]
     const int32_t* cu;    // ragged batches: cumulative draft lengths [B+1], else null
     long long total_draft;  // ragged batches: draft rows in the buffers
     long long row_stride; // elements
@@ -134,5 +136,11 @@ struct Params {
 // Return a hipError_t value (0 = success).
 int launch_stochastic(const Params& p, int dtype, bool vec, bool seq_resident, void* stream);
 int launch_greedy(const Params& p, int dtype, bool vec, bool seq_resident, void* stream);
+// Greedy draft-tree verification (row-split layout; rows_per_seq = N nodes).
+int launch_tree(const Params& p, int dtype, bool vec, void* stream);
+// Commit of a verified step (see sv_commit in specverify.h).
+int launch_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
+                  int32_t* seq_len, int32_t* history, long long history_stride, int capacity,
+                  int32_t* next_token, long long next_stride, void* stream);
 
 }  // namespace sv

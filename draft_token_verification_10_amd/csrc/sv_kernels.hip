@@ -1375,6 +1375,140 @@ __global__ __launch_bounds__(NT_FIN) void k_greedy_finish(Params p) {
 }
 
 // ------------------------------------------------------------------------
+// Greedy verification of a draft tree per sequence (N nodes; node 0 is the
+// root, parents[j] < j).  After the row statistics give the argmax g of every
+// node's row, one workgroup per sequence (one thread per node) decides:
+// node j is accepted when every edge on its root path matches (the child's
+// token equals the argmax of the parent's row).  Pointer jumping folds the
+// path in ceil(log2 N) rounds: anc[j] is the node the fold has reached,
+// ok[j] and dep[j] the AND of the edge tests and the edge count from j up to
+// anc[j].  The deepest accepted node wins, lowest index on ties.  A parent
+// outside [0, j) (a malformed tree) makes the node unaccepted.
+constexpr int kMaxTreeNodes = kMaxRowsPerSeq;
+
+struct TreeSmem {
+    int g[kMaxTreeNodes];
+    int par[kMaxTreeNodes];
+    int tok[kMaxTreeNodes];
+    int anc[kMaxTreeNodes];
+    int ok[kMaxTreeNodes];
+    int dep[kMaxTreeNodes];
+    Scratch<NT_FIN> sc;
+};
+
+__global__ __launch_bounds__(NT_FIN) void k_tree_finish(Params p) {
+    __shared__ TreeSmem sm;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int N = p.rows_per_seq, S = p.S;
+    const float* part = p.part + (size_t)b * N * S * 2;
+    const int32_t* par = p.parents + (size_t)b * N;
+    const int32_t* tok = p.tokens_in + (size_t)b * N;
+    for (int j = tid; j < N; j += NT_FIN) {
+        float best = part[(j * S) * 2];
+        int idx = __float_as_int(part[(j * S) * 2 + 1]);
+        for (int s = 1; s < S; ++s) {
+            const float m = part[(j * S + s) * 2];
+            if (m > best) {  // earlier slices hold lower indices: they win ties
+                best = m;
+                idx = __float_as_int(part[(j * S + s) * 2 + 1]);
+            }
+        }
+        sm.g[j] = idx;
+        sm.par[j] = par[j];
+        sm.tok[j] = tok[j];
+    }
+    __syncthreads();
+    for (int j = tid; j < N; j += NT_FIN) {
+        const int pj = sm.par[j];
+        const bool valid = j > 0 && pj >= 0 && pj < j;
+        sm.anc[j] = valid ? pj : 0;
+        sm.ok[j] = j == 0 ? 1 : (valid && sm.tok[j] == sm.g[pj]);
+        sm.dep[j] = j == 0 ? 0 : 1;
+    }
+    __syncthreads();
+    for (int span = 1; span < N; span <<= 1) {
+        int o[kMaxTreeNodes / NT_FIN], d[kMaxTreeNodes / NT_FIN], a2[kMaxTreeNodes / NT_FIN];
+#pragma unroll
+        for (int u = 0; u < kMaxTreeNodes / NT_FIN; ++u) {
+            const int j = tid + u * NT_FIN;
+            if (j < N) {
+                const int a = sm.anc[j];
+                o[u] = sm.ok[a];
+                d[u] = sm.dep[a];
+                a2[u] = sm.anc[a];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kMaxTreeNodes / NT_FIN; ++u) {
+            const int j = tid + u * NT_FIN;
+            if (j < N) {
+                sm.ok[j] &= o[u];
+                sm.dep[j] += d[u];
+                sm.anc[j] = a2[u];
+            }
+        }
+        __syncthreads();
+    }
+    // deepest accepted node, lowest index on ties: maximise dep * 2048 + (2047 - j)
+    int key = -1;
+    for (int j = tid; j < N; j += NT_FIN)
+        if (sm.ok[j]) key = max(key, sm.dep[j] * 2048 + (2047 - j));
+    {
+        const int lane = tid & 63, wave = tid >> 6;
+        key = wave_max_i(key);
+        if (lane == 0) sm.sc.j[wave] = key;
+        __syncthreads();
+        key = sm.sc.j[0];
+#pragma unroll
+        for (int w = 1; w < NT_FIN / 64; ++w) key = max(key, sm.sc.j[w]);
+    }
+    const int best = 2047 - (key & 2047);  // the root (key 2047) is always accepted
+    const int d = key >> 11;
+    int32_t* out_t = p.tokens_out + (size_t)b * N;
+    int32_t* out_p = p.path + (size_t)b * N;
+    for (int i = tid; i < N; i += NT_FIN)
+        if (i > d) {
+            out_t[i] = -1;
+            out_p[i] = -1;
+        }
+    if (tid == 0) {
+        // walk back from the winner: its ancestors are all accepted, so the
+        // parents on the way are valid and strictly decreasing
+        int j = best;
+        for (int i = d; i >= 0; --i) {
+            out_p[i] = j;
+            if (i > 0) out_t[i - 1] = sm.tok[j];
+            j = i > 0 ? sm.par[j] : 0;
+        }
+        out_t[d] = sm.g[best];
+        p.accept_len[b] = d;
+    }
+}
+
+// Commit of a verified step: one thread per sequence appends its emitted
+// tokens to its history (up to the capacity), advances its length and writes
+// the last emitted token into the next step's input slot.
+__global__ __launch_bounds__(256) void k_commit(const int32_t* __restrict__ accept_len,
+                                                const int32_t* __restrict__ tokens, int B, int W,
+                                                int32_t* seq_len, int32_t* history,
+                                                long long history_stride, int capacity,
+                                                int32_t* next_token, long long next_stride) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= B) return;
+    int a = accept_len[b];
+    a = a < 0 ? 0 : (a >= W ? W - 1 : a);  // keeps a malformed value inside the row
+    const int32_t* t = tokens + (size_t)b * W;
+    int L = seq_len[b];
+    if (L < 0) L = 0;
+    int32_t* h = history + (size_t)b * history_stride;
+    for (int j = 0; j <= a && L < capacity; ++j) h[L++] = t[j];
+    seq_len[b] = L;
+    next_token[(size_t)b * next_stride] = t[a];
+}
+
+// ------------------------------------------------------------------------
 template <typename K>
 static int launch1(K kernel, const Params& p, long long grid, int block, void* stream) {
     Params pc = p;
@@ -1418,6 +1552,28 @@ int launch_greedy(const Params& p, int dtype, bool vec, bool seq, void* stream) 
     if (dtype == 1)
         return vec ? launch_greedy_t<1, true>(p, seq, stream) : launch_greedy_t<1, false>(p, seq, stream);
     return vec ? launch_greedy_t<0, true>(p, seq, stream) : launch_greedy_t<0, false>(p, seq, stream);
+}
+
+template <int DT, bool VEC>
+static int launch_tree_t(const Params& p, void* stream) {
+    const long long items = (long long)p.B * p.rows_per_seq * p.S;
+    int e = launch1(k_row_stats<DT, VEC, false>, p, items, NT_ROW, stream);
+    if (e) return e;
+    return launch1(k_tree_finish, p, p.B, NT_FIN, stream);
+}
+
+int launch_tree(const Params& p, int dtype, bool vec, void* stream) {
+    if (dtype == 1) return vec ? launch_tree_t<1, true>(p, stream) : launch_tree_t<1, false>(p, stream);
+    return vec ? launch_tree_t<0, true>(p, stream) : launch_tree_t<0, false>(p, stream);
+}
+
+int launch_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
+                  int32_t* seq_len, int32_t* history, long long history_stride, int capacity,
+                  int32_t* next_token, long long next_stride, void* stream) {
+    hipLaunchKernelGGL(k_commit, dim3((unsigned)((B + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), accept_len, tokens, B, W, seq_len,
+                       history, history_stride, capacity, next_token, next_stride);
+    return (int)hipGetLastError();
 }
 
 }  // namespace sv

@@ -204,9 +204,59 @@ int sv_sample(const void* logits, const float* u, int B, int V, int64_t row_stri
               float temperature, int greedy, int32_t* tokens, void* workspace,
               size_t workspace_bytes, void* stream);
 
+/*
+ * Greedy verification of a draft tree per sequence: the Top-K tree of the
+ * EAGLE scheme (Perplexity, "Accelerating Sonar through speculation", section
+ * "EAGLE": several draft continuations are explored as a tree, the longest
+ * acceptable one is kept and the target adds one more token).
+ *   target_logits [B][N] rows: row j of sequence b (at (b*N + j) * row_stride)
+ *                 is the target's output at node j, i.e. its prediction of
+ *                 the token that follows node j's path (tree attention mask
+ *                 on the model side)
+ *   node_tokens   int32 [B][N]: the draft token of node j (node 0, the root,
+ *                 is the last committed token and is not verified)
+ *   parents       int32 [B][N]: parent of node j, in [0, j) for j >= 1;
+ *                 parents[b][0] = -1
+ *   accept_len    out int32 [B]: depth d of the winning node
+ *   tokens        out int32 [B][N]: the draft tokens along the root-to-winner
+ *                 path, then the argmax of the winner's row; -1 after
+ *   path          out int32 [B][N]: node indices root, ..., winner; -1 after
+ * Node j is accepted when its parent is and its token equals the argmax
+ * (lowest index on ties) of the parent's row; the deepest accepted node wins,
+ * lowest node index among equal depths.  A chain (parents[j] = j - 1) is
+ * sv_verify_greedy with k = N - 1.  1 <= N <= SV_MAX_ROWS_PER_SEQ.  A parent
+ * outside [0, j) is not checked on the host: that node is never accepted.
+ * Workspace: sv_workspace_bytes(B, N, 0, V).
+ */
+int sv_verify_greedy_tree(const void* target_logits, const int32_t* node_tokens,
+                          const int32_t* parents, int B, int N, int V, int64_t row_stride,
+                          int dtype, int32_t* accept_len, int32_t* tokens, int32_t* path,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Commit of a verified step on the GPU, so that the next step can be launched
+ * without the host reading accept_len first (Perplexity, same page, sections
+ * "MTP" and "Plánovanie MTP pre Jediný Token": the accepted tokens are shifted
+ * into place by kernels and the next draft runs on the same batch, the host
+ * learns the lengths in parallel).  For sequence b, with a = accept_len[b]
+ * and L = seq_len[b]:
+ *   history[b][L + j] = tokens[b][j] for j = 0..a while L + j < capacity
+ *   seq_len[b]        = min(L + a + 1, capacity)   (unchanged if L >= capacity)
+ *   next_token[b * next_stride] = tokens[b][a]     (the token the next step
+ *                                                    starts from)
+ *   accept_len [B], tokens [B][W] as the verification calls write them (W =
+ *   k + 1, k_max + 1 or N); seq_len int32 [B] in/out; history int32 rows of
+ *   history_stride >= capacity entries.  An accept_len outside [0, W - 1] or
+ *   a negative seq_len is clamped into range (undefined result, no
+ *   out-of-bounds access).  No workspace.
+ */
+int sv_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W, int32_t* seq_len,
+              int32_t* history, int64_t history_stride, int capacity, int32_t* next_token,
+              int64_t next_stride, void* stream);
+
 /* Workspace bytes that suffice for any entry point at this shape (G = 1 for
- * stochastic, ragged (k = k_max) and sampling (k = 0) calls).  Returns 0 for
- * an invalid shape. */
+ * stochastic, ragged (k = k_max) and sampling (k = 0) calls; G = N, k = 0 for
+ * tree verification).  Returns 0 for an invalid shape. */
 size_t sv_workspace_bytes(int B, int G, int k, int V);
 
 /* Static, human-readable text for a status code. */

@@ -36,8 +36,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["sv_sample", "sv_status_string", "sv_verify_greedy",
-                     "sv_verify_greedy_ragged", "sv_verify_stochastic",
+    assert names == ["sv_commit", "sv_sample", "sv_status_string", "sv_verify_greedy",
+                     "sv_verify_greedy_ragged", "sv_verify_greedy_tree", "sv_verify_stochastic",
                      "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), n
@@ -251,3 +251,55 @@ def test_sample_checks(lib):
     assert sample(lib, dtype=9) == SV_ERR_DTYPE
     assert sample(lib, V=0) == SV_ERR_SHAPE
     assert sample(lib, B=0, t=None, u=None, tok=None, ws=None, wsb=0) == SV_OK
+
+
+def tree(lib, **kw):
+    args = dict(t=A, x=A, par=A, B=2, N=5, V=100, rs=100, dtype=1, al=A, tok=A, path=A, ws=WS,
+                wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.sv_verify_greedy_tree(args["t"], args["x"], args["par"], args["B"], args["N"],
+                                     args["V"], args["rs"], args["dtype"], args["al"],
+                                     args["tok"], args["path"], args["ws"], args["wsb"],
+                                     args["stream"])
+
+
+def commit(lib, **kw):
+    args = dict(al=A, tok=A, B=4, W=9, sl=A, h=A, hs=100, cap=100, nx=A, ns=1, stream=None)
+    args.update(kw)
+    return lib.sv_commit(args["al"], args["tok"], args["B"], args["W"], args["sl"], args["h"],
+                         args["hs"], args["cap"], args["nx"], args["ns"], args["stream"])
+
+
+@pytest.mark.parametrize("field", ["t", "x", "par", "al", "tok", "path", "ws"])
+def test_tree_null(lib, field):
+    assert tree(lib, **{field: None}) == SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(N=0), dict(N=1025), dict(V=0), dict(rs=99)])
+def test_tree_shape(lib, kw):
+    assert tree(lib, **kw) == SV_ERR_SHAPE
+
+
+def test_tree_other_checks(lib):
+    assert tree(lib, dtype=5) == SV_ERR_DTYPE
+    assert tree(lib, wsb=0) == SV_ERR_WORKSPACE
+    assert tree(lib, B=0, t=None, x=None, par=None, al=None, tok=None, path=None, ws=None,
+                wsb=0) == SV_OK
+    # the workspace bound for a tree: G = N nodes, k = 0
+    assert lib.sv_workspace_bytes(256, 64, 0, 128256) >= 256 * 64 * 8
+    assert lib.sv_workspace_bytes(300, 1, 0, 1000) > 0  # a root-only tree at a large batch
+
+
+@pytest.mark.parametrize("field", ["al", "tok", "sl", "h", "nx"])
+def test_commit_null(lib, field):
+    assert commit(lib, **{field: None}) == SV_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(W=0), dict(cap=-1), dict(hs=50),
+                                dict(ns=0)])
+def test_commit_shape(lib, kw):
+    assert commit(lib, **kw) == SV_ERR_SHAPE
+
+
+def test_commit_empty(lib):
+    assert commit(lib, B=0, al=None, tok=None, sl=None, h=None, nx=None) == SV_OK
