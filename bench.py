@@ -18,6 +18,10 @@ Modes:
               (sv_verify_greedy_ragged) objects beside it
   sample      sv_sample of one token per sequence from target row 0, with a
               "greedy" (argmax) object beside it
+  tree        sv_verify_greedy_tree on B=32 sequences of a fixed 64-node
+              EAGLE-style draft tree (V=128256, bf16)
+  commit      sv_commit of the workload's verified step (B sequences, k+1
+              token slots): a launch-bound kernel, timed on its own
 
 Inputs smaller than 512 MB are replicated and the copies rotated from call to
 call, so that no call finds its logits in the 256 MB last-level cache (cold
@@ -71,6 +75,19 @@ def algorithmic_bytes(spec, mode: str, kb=None, greedy=False) -> int:
     if mode == "sample":
         return B * V * s + (0 if greedy else 4 * B) + 4 * B
     raise ValueError(mode)
+
+
+def tree_bytes(B: int, N: int, V: int, s: int) -> int:
+    """Every node row once, node tokens and parents in, accept_len, tokens and
+    path out."""
+    return B * N * V * s + 8 * B * N + 4 * B + 8 * B * N
+
+
+def commit_bytes(accept, W: int) -> int:
+    """accept_len, the token rows and seq_len read; the appended tokens,
+    seq_len and the next token written."""
+    B = len(accept)
+    return 4 * B + 4 * B * W + 4 * B + 4 * int(sum(int(a) + 1 for a in accept)) + 4 * B + 4 * B
 
 
 def kernel_name(spec, mode: str, diagnostics=True, greedy=False) -> str:
@@ -148,6 +165,33 @@ def per_call_us(fns, steps: int, torch):
     return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
 
 
+def graph_us(fns, calls: int, replays: int, torch):
+    """Device time per call without host launch overhead: `calls` calls
+    (cycling through `fns`) captured once in a HIP graph on a side stream of
+    default priority, replayed `replays` times between two events."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):  # workspaces are allocated here, outside the capture
+            fns[i % len(fns)]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(calls):
+            fns[i % len(fns)]()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (calls * replays)
+
+
 def n_copies(input_bytes: int, forced) -> int:
     if forced is not None:
         return max(1, forced)
@@ -212,13 +256,103 @@ def side(spec, fns, nbytes, kern, traffic_key, args, torch, extra=None):
     return out
 
 
+def bench_tree(args, torch, dev, binding, workloads):
+    import numpy as np
+    print("# generating the draft-tree batch", file=sys.stderr, flush=True)
+    tb = workloads.tree_batch()
+    B, N, V = tb.target.shape
+    s_b = 2 if tb.dtype == 1 else 4
+    nc = n_copies(tb.target.nbytes, args.copies)
+    t0 = logits_to_device(tb.target, tb.dtype, torch, dev)
+    ts = [t0] + [t0.clone() for _ in range(nc - 1)]
+    x = torch.from_numpy(tb.node_tokens).to(dev)
+    par = torch.from_numpy(tb.parents).to(dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, N), dtype=torch.int32, device=dev)
+    path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    fns = [(lambda t=t: binding.sv_verify_greedy_tree(t, x, par, accept_len=acc, tokens=tok,
+                                                      path=path)) for t in ts]
+    ms, wall = time_calls(fns, args.steps, args.warmup, torch)
+    nbytes = tree_bytes(B, N, V, s_b)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "verified seqs/sec + achieved HBM GB/s (% of peak), greedy draft tree",
+        "value": round(B / (ms * 1e-3), 1), "unit": "seqs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if tb.dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": f"tree_B{B}_N{N}_V{V}_bf16", "B": B, "N": N, "V": V,
+                   "tree_levels": list(workloads.TREE_LEVELS), "mode": "tree",
+                   "input_copies_rotated": nc},
+        "achieved_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("tree"), "algorithmic_bytes": nbytes,
+                     "kernel": "k_row_stats"},
+        "wall_s_timed": round(wall, 3),
+        "per_call_us": per_call_us(fns, min(args.steps, 100), torch),
+        "mean_accepted_depth": round(float(acc.float().mean().item()), 4),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import svo
+        result["cpu_baseline"] = cpu_baseline(
+            lambda: svo.verify_greedy_tree(tb.target, tb.node_tokens, tb.parents, B=B, N=N, V=V),
+            B, f"the draft-tree batch (B={B}, N={N})")
+    print(json.dumps(result), flush=True)
+
+
+def bench_commit(args, torch, dev, binding, workloads, spec):
+    """The commit of workload `spec`'s greedy verification outputs."""
+    import numpy as np
+    print(f"# generating workload {spec.index} for its verified step", file=sys.stderr, flush=True)
+    batch = workloads.make(spec.index)
+    B, k = spec.B, spec.k
+    t = logits_to_device(batch.target, spec.dtype, torch, dev)
+    x = torch.from_numpy(batch.draft_tokens).to(dev)
+    acc, tok = binding.sv_verify_greedy(t, x)[:2]
+    cap = 16384  # room for every commit of the run: none is cut short by the capacity
+    hist = torch.zeros((B, cap), dtype=torch.int32, device=dev)
+    seq_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    ids = torch.zeros((B, k + 1), dtype=torch.int32, device=dev)
+
+    def step():
+        binding.sv_commit(acc, tok, seq_len, hist, ids[:, 0])
+
+    a_host = acc.cpu().numpy()
+    nbytes = commit_bytes(a_host, k + 1)
+    # Device time: 50 commits captured in a graph, replayed 20 times.
+    calls, replays = 50, 20
+    seq_len.zero_()
+    us_graph = graph_us([step], calls, replays, torch)
+    seq_len.zero_()
+    ms, wall = time_calls([step], min(args.steps, (cap - 1) // (k + 1) - args.warmup),
+                          args.warmup, torch)
+    result = {
+        "metric": "commit of a verified step: µs per call on the device (graph replay)",
+        "value": round(us_graph, 3), "unit": "us", "n_gpus": 1,
+        "steps": calls, "warmup": 3, "ms_per_step": round(us_graph * 1e-3, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": spec.name, "B": B, "W": k + 1, "mode": "commit"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (us_graph * 1e-6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (us_graph * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+                     "traffic": None, "algorithmic_bytes": nbytes, "kernel": "k_commit"},
+        "eager_us_per_call": round(ms * 1e3, 3),
+        "note": "a launch-bound kernel: the eager figure is the Python binding's call rate",
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--mode", choices=["stochastic", "greedy", "ragged", "sample"], default=None)
+    ap.add_argument("--mode", choices=["stochastic", "greedy", "ragged", "sample", "tree",
+                                       "commit"], default=None)
     ap.add_argument("--copies", type=int, default=None,
                     help="input copies rotated between calls (default: enough to exceed 600 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -246,8 +380,12 @@ def main():
 
     from draft_token_verification_10_amd import binding, workloads
 
+    if args.mode == "tree":
+        return bench_tree(args, torch, dev, binding, workloads)
     spec = workloads.SPECS[args.workload]
     mode = args.mode or spec.modes[0]
+    if mode == "commit":
+        return bench_commit(args, torch, dev, binding, workloads, spec)
     if mode in ("ragged",) and (spec.G != 1 or spec.index == 4):
         sys.exit("ragged mode needs a single-candidate stochastic workload")
     print(f"# generating workload {spec.index} ({spec.name}), mode {mode}", file=sys.stderr,
@@ -340,6 +478,10 @@ def main():
     ms, wall = time_calls(fns, args.steps, args.warmup, torch)
     result = line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_cfg)
     result["per_call_us"] = per_call_us(fns, min(args.steps, 100), torch)
+    if ms < 0.05:
+        # launch-bound: the device time of a call without the binding's host
+        # overhead (20 calls captured in a graph, 10 replays)
+        result["graph_us_per_call"] = round(graph_us(fns, 20, 10, torch), 2)
     if nc > 1:
         ms_w, _ = time_calls(fns[:1], args.steps, args.warmup, torch)
         result["warm"] = {"ms_per_step": round(ms_w, 5),

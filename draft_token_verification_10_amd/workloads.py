@@ -23,7 +23,8 @@ Two derived inputs reuse a workload's rows: a ragged batch (``ragged``), in
 which sequence b keeps only its first k_b ~ U{1..k} draft positions (drawn
 from a seventh stream), packed without gaps; and a sampling batch
 (``sample_rows``), the first target row of every sequence with its sample
-uniform.
+uniform.  A draft-tree batch (``tree_batch``) holds a fixed 64-node
+EAGLE-style tree per sequence.
 
 The workloads:
 
@@ -257,6 +258,70 @@ def ragged(batch: Batch) -> RaggedBatch:
         ua[d0:d0 + k] = batch.u_accept[b, :k]
     return RaggedBatch(spec=s, k_max=s.k, kb=kb, cu=cu, target=target, draft=draft,
                        draft_tokens=x, u_accept=ua, u_sample=batch.u_sample.copy())
+
+
+# A fixed 64-node draft tree in the style of EAGLE's Top-K trees: level sizes
+# 1, 8, 16, 16, 12, 8, 3; node i of a level hangs under node i mod m of the
+# previous level (m nodes), so the earliest (most probable) nodes of a level
+# carry the most children.
+TREE_LEVELS = (1, 8, 16, 16, 12, 8, 3)
+
+
+def tree_parents(levels=TREE_LEVELS) -> np.ndarray:
+    par = [-1]
+    prev = [0]
+    for size in levels[1:]:
+        cur = []
+        for i in range(size):
+            par.append(prev[i % len(prev)])
+            cur.append(len(par) - 1)
+        prev = cur
+    return np.array(par, dtype=np.int32)
+
+
+@dataclass
+class TreeBatch:
+    """target: [B][N][V] (row j: the target's output at node j); node_tokens,
+    parents: int32 [B][N]."""
+    V: int
+    dtype: int
+    target: np.ndarray
+    node_tokens: np.ndarray
+    parents: np.ndarray
+
+
+def tree_batch(B: int = 32, V: int = 128256, dtype: int = BF16, follow: float = 0.8,
+               seed: int = 10_005) -> TreeBatch:
+    """B sequences with the fixed 64-node tree; target rows ~ N(0, 3^2)
+    (seeded per sequence); the first child of every node carries the argmax of
+    its parent's row with probability `follow` (a drafter whose top choice is
+    often right), other children a uniform token."""
+    par = tree_parents()
+    N = len(par)
+    first = np.zeros(N, bool)
+    seen = set()
+    for j in range(1, N):
+        if par[j] not in seen:
+            first[j] = True
+            seen.add(par[j])
+
+    def one(b):
+        r = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(0, b)))
+        t = round_logits(r.standard_normal((N, V)) * 3.0, dtype)
+        g = np.argmax(as_f64(t, dtype), axis=-1)
+        x = r.integers(0, V, size=N).astype(np.int32)
+        follow_draw = r.random(N)
+        for j in range(1, N):
+            if first[j] and follow_draw[j] < follow:
+                x[j] = g[par[j]]
+        x[0] = -1
+        return t, x
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(one, range(B)))
+    return TreeBatch(V=V, dtype=dtype, target=np.stack([p[0] for p in parts]),
+                     node_tokens=np.stack([p[1] for p in parts]),
+                     parents=np.tile(par, (B, 1)))
 
 
 def sample_rows(batch: Batch):

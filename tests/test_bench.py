@@ -54,3 +54,20 @@ def test_several_gpus_refused():
     p = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True,
                        text=True, cwd=bench.ROOT, timeout=120)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_tree_workload_shape():
+    par = W.tree_parents()
+    assert len(par) == sum(W.TREE_LEVELS) == 64
+    assert par[0] == -1 and all(0 <= par[j] < j for j in range(1, 64))
+    depth = [0] * 64
+    for j in range(1, 64):
+        depth[j] = depth[par[j]] + 1
+    assert [depth.count(d) for d in range(len(W.TREE_LEVELS))] == list(W.TREE_LEVELS)
+    tb = W.tree_batch(B=2, V=300)
+    assert tb.target.shape == (2, 64, 300) and tb.node_tokens[:, 0].tolist() == [-1, -1]
+    assert bench.tree_bytes(32, 64, 128256, 2) == 32 * 64 * 128256 * 2 + 16 * 32 * 64 + 4 * 32
+
+
+def test_commit_bytes():
+    assert bench.commit_bytes([0, 2], 3) == 4 * 2 + 4 * 6 + 4 * 2 + 4 * 4 + 4 * 2 + 4 * 2

@@ -56,7 +56,8 @@ TREE_CASES = [
 def test_tree(case):
     B, N, V, dtype, pad, unal, ties, deep = case
     print(f"tree case {case}", flush=True)
-    t, x, par = make_tree(hash(case) & 0xFFFF, B, N, V, dtype, ties, deep)
+    t, x, par = make_tree(hash(case) & 0xFFFF, B, N, V, dtype, ties, deep,
+                          follow=0.97 if deep else 0.7)
     tt, th, rs = logits_to_device(t, dtype, pad, unal)
     a, tok, path = binding.sv_verify_greedy_tree(tt, dev(x), dev(par))
     torch.cuda.synchronize()
@@ -64,7 +65,8 @@ def test_tree(case):
     assert np.array_equal(a.cpu().numpy(), o["accept_len"])
     assert np.array_equal(tok.cpu().numpy(), o["tokens"])
     assert np.array_equal(path.cpu().numpy(), o["path"])
-    print("mean accepted depth", o["accept_len"].mean(), "max", o["accept_len"].max())
+    if deep:  # long accepted paths exercise many pointer-jumping rounds
+        assert o["accept_len"].max() >= 8, o["accept_len"]
 
 
 @pytest.mark.parametrize("B,k", [(7, 5), (300, 3)])
