@@ -167,3 +167,55 @@ def test_decode_loop_on_device(mode):
     assert sl.min() >= n
     for b in range(B):
         assert list(h[b, :n]) == _greedy_decode(T, s0[b], n), b
+
+
+def test_graph_replays_match_eager():
+    """The library's launches captured in a HIP graph (as bench.py does for
+    launch-bound calls): several replays, with eager work and synchronisation
+    in between, each give exactly the eager outputs.  Covers the stochastic
+    row-split and sequence-resident layouts, sampling and commit."""
+    from tests.test_gpu_parity import make_stochastic
+    cases = []
+    for B in (5, 200):
+        t, d, x, ua, us = make_stochastic(B + 11, B, 3, 4103, W.BF16, 1.0)
+        tt, _, _ = logits_to_device(t, W.BF16)
+        dt, _, _ = logits_to_device(d, W.BF16)
+        cases.append((tt, dt, dev(x), dev(ua), dev(us)))
+    rows, _, _ = logits_to_device(W.round_logits(
+        np.random.default_rng(3).standard_normal((64, 5000)) * 3, W.BF16), W.BF16)
+    u = dev(W.exact_uniforms(np.random.default_rng(4), 64))
+    outs = {}
+
+    def run():
+        res = []
+        for i, (tt, dt, x, ua, us) in enumerate(cases):
+            a, tok = binding.sv_verify_stochastic(tt, dt, x, ua, us, 1.0,
+                                                  accept_len=outs[f"a{i}"],
+                                                  tokens=outs[f"t{i}"])
+            res += [a, tok]
+        res.append(binding.sv_sample(rows, u, 1.0, tokens=outs["y"]))
+        return res
+
+    for i, (tt, _, _, _, _) in enumerate(cases):
+        outs[f"a{i}"] = torch.full((tt.shape[0],), -9, dtype=torch.int32, device=DEV)
+        outs[f"t{i}"] = torch.full((tt.shape[0], 4), -9, dtype=torch.int32, device=DEV)
+    outs["y"] = torch.full((64,), -9, dtype=torch.int32, device=DEV)
+    eager = [r.clone() for r in run()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # workspaces for this stream are allocated outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        captured = run()
+    for rep in range(3):
+        for o in outs.values():
+            o.fill_(-9)           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, c in zip(eager, captured):
+            assert torch.equal(e, c), f"replay {rep} differs from the eager call"
