@@ -791,7 +791,7 @@ struct GreedyFin {
     int a;
     int c;
     int g[kMaxRowsPerSeq];           // argmax of every row of the sequence
-    int cand_a[kMaxRowsPerSeq / 2];  // G <= kMaxRowsPerSeq / (k+1), k >= 1
+    int cand_a[kMaxRowsPerSeq];      // G <= kMaxRowsPerSeq / (k+1), k >= 0
 };
 
 // Needs g[] of every row of sequence b in LDS (after a barrier).

@@ -146,6 +146,15 @@ STOCH_CASES = [
     (300, 4, 2053, W.BF16, 1.0, 8, False, "equal"),
     (257, 8, 9, W.F32, 1.0, 0, False, "close"),
     (196, 2, 20011, W.BF16, 1.2, 0, False, "onehot"),
+    # the maximum draft length, both layouts
+    (3, 64, 1000, W.BF16, 1.0, 0, False, "close"),
+    (192, 64, 300, W.F32, 1.0, 0, False, "close"),
+    # extreme temperatures (exponents far from 0 after scaling)
+    (6, 4, 50000, W.BF16, 0.05, 0, False, None),
+    (200, 3, 4103, W.F32, 20.0, 0, False, None),
+    (7, 3, 2053, W.F32, 0.02, 0, True, "neginf"),
+    # a vocabulary past a million entries
+    (2, 1, 1048583, W.BF16, 1.0, 0, False, None),
 ]
 
 
@@ -198,6 +207,9 @@ GREEDY_CASES = [
     (256, 1, 8, 4103, W.F32, 0, True, True),
     (200, 1, 2, 1000, W.BF16, 2, False, True),
     (192, 1, 3, 20011, W.BF16, 0, False, False),
+    # the largest sequence: 16 candidates of 64 rows (1024 rows), and k = 64
+    (2, 16, 63, 700, W.BF16, 0, False, True),
+    (200, 1, 64, 500, W.F32, 0, True, True),
 ]
 
 
@@ -209,6 +221,22 @@ def test_greedy_small(case):
     t, x = make_greedy(hash(case) & 0xFFFF, B, G, k, V, dtype, ties)
     rep, _ = run_greedy(t, x, dtype, pad, unal)
     assert rep.ok(), rep.summary()
+
+
+def test_greedy_many_candidates_no_drafts():
+    """k = 0 with the most candidates a sequence may have (G = 1024): every
+    candidate accepts nothing, candidate 0 wins, its row 0's argmax is the
+    token."""
+    rng = np.random.default_rng(17)
+    B, G, V = 3, 1024, 300
+    t = rng.integers(-3, 3, size=(B, G, 1, V)).astype(np.float32)
+    tt, th, rs = logits_to_device(t, W.F32)
+    x = torch.empty((B, G, 0), dtype=torch.int32, device=DEV)
+    a, tok, bc = binding.sv_verify_greedy(tt, x)
+    torch.cuda.synchronize()
+    want = svo.sample(np.ascontiguousarray(t[:, 0, 0]), None, B=B, V=V, greedy=True)
+    assert np.all(a.cpu().numpy() == 0) and np.all(bc.cpu().numpy() == 0)
+    assert np.array_equal(tok.cpu().numpy()[:, 0], want)
 
 
 def test_greedy_all_neginf_row():
