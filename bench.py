@@ -7,7 +7,8 @@ HBM: every row of the hot path (row statistics over all logits, acceptance
 ratios, accept-prefix scan, corrective/bonus draw, outputs; plus candidate
 selection for the multi-candidate workload).  The default workload is B=256
 sequences, k=8 draft tokens, V=128256, bfloat16 logits, stochastic mode.
-Prints one JSON line.
+Prints one JSON line.  "dtype" is the arithmetic type of the kernels (f32:
+bf16 logits are widened on load); the logit type is in "config".
 
 Modes:
   stochastic  sv_verify_stochastic (p/q diagnostics on: every row is read);
@@ -200,26 +201,34 @@ def n_copies(input_bytes: int, forced) -> int:
     return min(MAX_COPIES, math.ceil(COLD_BYTES / max(1, input_bytes)))
 
 
-def cpu_baseline(run, B: int, what: str, reps: int = 3):
-    """The float64 oracle as it stands, on the host cores, over the whole
-    batch (median of `reps`)."""
+def cpu_baseline(run, B: int, what: str, min_reps: int = 3, target_s: float = 10.0,
+                 max_s: float = 30.0):
+    """The float64 oracle as it stands, on the host cores: whole-batch passes
+    repeated until about `target_s` seconds of work (at least `min_reps`
+    passes, never starting one past `max_s`); the median pass is reported."""
     from oracle import svo
     times = []
-    for _ in range(reps):
+    t_start = time.perf_counter()
+    while True:
         t0 = time.perf_counter()
         run()
         times.append(time.perf_counter() - t0)
+        spent = time.perf_counter() - t_start
+        if len(times) >= min_reps and (spent >= target_s or spent + times[-1] > max_s):
+            break
     times.sort()
     med = times[len(times) // 2]
     return {"value": round(B / med, 2), "unit": "seqs/s", "cores": svo.num_threads(),
             "kind": "oracle",
-            "sample": f"all {B} sequences of {what}, median of {reps} runs, {med:.2f} s each"}
+            "sample": f"all {B} sequences of {what} per pass, {len(times)} passes "
+                      f"({sum(times):.1f} s), median pass {med:.3f} s"}
 
 
 def line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_config=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     cfg = {"workload": spec.name, "B": spec.B, "k": spec.k, "V": spec.V, "G": spec.G,
-           "mode": mode, "temperature": spec.tau}
+           "logits": "bf16" if spec.dtype == 1 else "f32", "mode": mode,
+           "temperature": spec.tau}
     cfg.update(extra_config or {})
     return {
         "metric": "verified seqs/sec + achieved HBM GB/s (% of peak), B=256 k=8 V=128256 bf16",
@@ -232,7 +241,7 @@ def line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_config=Non
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if spec.dtype == 1 else "f32",
+        "dtype": "f32",
         "data": "synthetic",
         "config": cfg,
         "achieved_GBps": round(gbs, 1),
@@ -280,8 +289,9 @@ def bench_tree(args, torch, dev, binding, workloads):
         "value": round(B / (ms * 1e-3), 1), "unit": "seqs/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if tb.dtype == 1 else "f32", "data": "synthetic",
+        "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"tree_B{B}_N{N}_V{V}_bf16", "B": B, "N": N, "V": V,
+                   "logits": "bf16" if tb.dtype == 1 else "f32",
                    "tree_levels": list(workloads.TREE_LEVELS), "mode": "tree",
                    "input_copies_rotated": nc},
         "achieved_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
