@@ -91,13 +91,19 @@ def commit_bytes(accept, W: int) -> int:
     return 4 * B + 4 * B * W + 4 * B + 4 * int(sum(int(a) + 1 for a in accept)) + 4 * B + 4 * B
 
 
-def kernel_name(spec, mode: str, diagnostics=True, greedy=False) -> str:
-    """The kernel that dominates a call: one workgroup per sequence for large
-    single-candidate batches, else the row-statistics kernel."""
+def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -> str:
+    """The kernel that dominates a call, following the library's layout
+    choice: one workgroup per sequence for large single-candidate batches
+    (not for plain sampling, nor for ragged batches of unequal lengths read
+    in full), else the row-statistics kernel."""
     if spec.G == 1 and spec.B >= 192:
         if greedy or mode == "greedy":
             return "k_greedy_seq"
-        return "k_stochastic_seq" if diagnostics else "k_stochastic_seq_exit"
+        if mode == "sample":
+            return "k_row_stats"
+        if not diagnostics:
+            return "k_stochastic_seq_exit"
+        return "k_stochastic_seq" if uniform else "k_row_stats"
     return "k_row_stats"
 
 
@@ -464,7 +470,7 @@ def main():
         fns_g = [(lambda t=t: binding.sv_verify_greedy_ragged(t, x, cu, k, accept_len=accept,
                                                               tokens=tokens)) for t in ts]
         nbytes = algorithmic_bytes(spec, "ragged", rb.kb)
-        kern = kernel_name(spec, "stochastic")
+        kern = kernel_name(spec, "ragged", uniform=bool((rb.kb == spec.k).all()))
         traffic_key = f"{spec.index}/ragged"
         extra_cfg = {"draft_len": "k_b ~ U{1..k}", "total_draft": int(rb.cu[-1]),
                      "mean_k_b": round(float(rb.kb.mean()), 4)}
@@ -478,7 +484,7 @@ def main():
         fns = [(lambda t=t: binding.sv_sample(t, ud, spec.tau, tokens=ytok)) for t in ts]
         fns_g = [(lambda t=t: binding.sv_sample(t, None, greedy=True, tokens=ytok)) for t in ts]
         nbytes = algorithmic_bytes(spec, "sample")
-        kern = kernel_name(spec, "sample", diagnostics=False)
+        kern = kernel_name(spec, "sample")
         traffic_key = f"{spec.index}/sample"
         extra_cfg = {"rows": "target row 0 of every sequence"}
     extra_cfg["input_copies_rotated"] = nc

@@ -71,3 +71,15 @@ def test_tree_workload_shape():
 
 def test_commit_bytes():
     assert bench.commit_bytes([0, 2], 3) == 4 * 2 + 4 * 6 + 4 * 2 + 4 * 4 + 4 * 2 + 4 * 2
+
+
+def test_kernel_names_follow_layouts():
+    s2, s1 = W.SPECS[2], W.SPECS[1]
+    assert bench.kernel_name(s2, "stochastic") == "k_stochastic_seq"
+    assert bench.kernel_name(s2, "stochastic", diagnostics=False) == "k_stochastic_seq_exit"
+    assert bench.kernel_name(s2, "greedy") == "k_greedy_seq"
+    assert bench.kernel_name(s2, "ragged", uniform=False) == "k_row_stats"
+    assert bench.kernel_name(s2, "ragged", uniform=True) == "k_stochastic_seq"
+    assert bench.kernel_name(s2, "sample") == "k_row_stats"
+    assert bench.kernel_name(s2, "sample", greedy=True) == "k_greedy_seq"
+    assert bench.kernel_name(s1, "stochastic") == "k_row_stats"
