@@ -303,3 +303,21 @@ def test_commit_shape(lib, kw):
 
 def test_commit_empty(lib):
     assert commit(lib, B=0, al=None, tok=None, sl=None, h=None, nx=None) == SV_OK
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/specverify.h compiles as C99 with warnings as errors, and a C
+    program links against libspecverify and gets the documented statuses."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no host C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(LIB_PATH)
+    exe = tmp_path / "abi_check"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_check.c"),
+                    "-L", libdir, "-lspecverify", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout, r.stderr)
