@@ -29,6 +29,8 @@ The facts:
 from __future__ import annotations
 
 import itertools
+import json
+import os
 
 import numpy as np
 
@@ -325,59 +327,58 @@ def pin_greedy_bf16_ties(lib):
 
 # ---------------------------------------------------------- closed forms ----
 
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_value(v):
+    if v == "-inf":
+        return -np.inf
+    if v == "ln3/2":
+        return float(np.float32(np.log(3.0) / 2))
+    if isinstance(v, list):
+        return [_golden_value(x) for x in v]
+    return v
+
+
+def load_closed_forms():
+    """The hand-worked cases of tests/golden/closed_forms.json as arrays."""
+    with open(os.path.join(GOLDEN_DIR, "closed_forms.json")) as f:
+        doc = json.load(f)
+    cases = []
+    for c in doc["cases"]:
+        cases.append(dict(
+            name=c["name"], oracle_only=c.get("oracle_only", False), B=c["B"], k=c["k"],
+            V=c["V"], tau=c["temperature"], expect=c["expect"],
+            t=np.array(_golden_value(c["target"]), np.float32),
+            d=np.array(_golden_value(c["draft"]), np.float32),
+            x=np.array(c["draft_tokens"], np.int32),
+            ua=np.array(c["u_accept"], np.float32),
+            us=np.array(c["u_sample"], np.float32),
+            force=None if c.get("force") is None else np.array(c["force"], np.int8)))
+    return cases
+
+
+def check_closed_form(case, accept_len, tokens, px=None, qx=None):
+    e = case["expect"]
+    assert list(accept_len) == e["accept_len"], case["name"]
+    if "tokens" in e:
+        assert np.asarray(tokens).tolist() == e["tokens"], case["name"]
+    if "tokens_row1" in e:
+        assert np.asarray(tokens)[1].tolist() == e["tokens_row1"], case["name"]
+    tol = e.get("px_tol", 0.0)
+    if px is not None and "px" in e:
+        assert np.all(np.abs(np.asarray(px, np.float64) - np.array(e["px"])) <= tol), case["name"]
+    if qx is not None and "qx" in e:
+        assert np.all(np.asarray(qx, np.float64) == np.array(e["qx"])), case["name"]
+
+
 def pin_closed_forms(lib):
-    """Cases worked by hand with dyadic probabilities (exact in binary)."""
-    ninf = -np.inf
-    # V=2, k=1.  target row 0 = [0, 0] -> p0 = [1/2, 1/2]; draft = [0, -inf] ->
-    # q0 = [1, 0]; draft token 0: p/q = 1/2.  u = 1/4 accepts, u = 3/4 rejects.
-    # Residual max(0, p0 - q0) = [0, 1/2] -> always token 1.
-    # Target row 1 = [0, 0, ...]: bonus p1 = [1/2, 1/2]; r = 0.75 -> token 1.
-    t = np.array([[[0, 0], [0, 0]]] * 2, np.float32)
-    d = np.array([[[0, ninf]]] * 2, np.float32)
-    X = np.zeros((2, 1), np.int32)
-    u = np.array([[0.25], [0.75]], np.float32)
-    r = np.array([0.75, 0.0], np.float32)
-    o = svo.verify_stochastic(t, d, X, u, r, B=2, k=1, V=2, lib=lib)
-    assert o["accept_len"].tolist() == [1, 0]
-    assert o["tokens"].tolist() == [[0, 1], [1, -1]]
-    assert o["px"][:, 0].tolist() == [0.5, 0.5] and o["qx"][:, 0].tolist() == [1.0, 1.0]
-    # V=4 bonus from p = [1/4]*4: cumulative 1/4, 1/2, 3/4, 1.  The first
-    # cumulative strictly above r: r=0 -> 0, r=1/4 -> 1, r=0.6 -> 2, r=3/4 -> 3.
-    B = 4
-    t = np.zeros((B, 2, 4), np.float32)
-    d = np.zeros((B, 1, 4), np.float32)
-    X = np.zeros((B, 1), np.int32)
-    u = np.zeros((B, 1), np.float32)
-    r = np.array([0.0, 0.25, 0.6, 0.75], np.float32)
-    o = svo.verify_stochastic(t, d, X, u, r, B=B, k=1, V=4, lib=lib)
-    assert o["accept_len"].tolist() == [1] * 4
-    assert o["tokens"][:, 1].tolist() == [0, 1, 2, 3]
-    # temperature 1/2 doubles logits: target [ln 3 /2, 0] at tau=1/2 behaves
-    # like [ln 3, 0] -> p = [3/4, 1/4] (up to the rounding of ln 3 in float32);
-    # draft [0, 0] -> q = [1/2, 1/2]; token 1: p/q = 1/2.  u = 0.49 accepts,
-    # u = 0.51 rejects; residual max(0, p - q) = [1/4, 0] -> token 0.
-    l3 = np.float32(np.log(3.0) / 2)
-    t = np.array([[[l3, 0], [0, 0]]] * 2, np.float32)
-    d = np.zeros((2, 1, 2), np.float32)
-    X = np.ones((2, 1), np.int32)
-    u = np.array([[0.49], [0.51]], np.float32)
-    r = np.array([0.9, 0.9], np.float32)
-    o = svo.verify_stochastic(t, d, X, u, r, B=2, k=1, V=2, temperature=0.5, lib=lib)
-    assert o["accept_len"].tolist() == [1, 0]
-    assert o["tokens"][1].tolist() == [0, -1]
-    assert abs(o["px"][0, 0] - 0.25) < 1e-7 and o["qx"][0, 0] == 0.5
-    # a draft token outside the vocabulary has probability 0 and is rejected
-    t = np.zeros((1, 2, 4), np.float32)
-    d = np.zeros((1, 1, 4), np.float32)
-    o = svo.verify_stochastic(t, d, np.array([[7]], np.int32), np.zeros((1, 1), np.float32),
-                              np.array([0.1], np.float32), B=1, k=1, V=4, lib=lib)
-    assert o["accept_len"][0] == 0 and o["px"][0, 0] == 0 and o["qx"][0, 0] == 0
-    # p == q: residual is zero everywhere; the oracle then samples p itself
-    # (here uniform over 4): r = 0.6 -> token 2.
-    f = np.array([[svo.FORCE_REJECT]], np.int8)
-    o = svo.verify_stochastic(t, d, np.zeros((1, 1), np.int32), np.zeros((1, 1), np.float32),
-                              np.array([0.6], np.float32), B=1, k=1, V=4, force=f, lib=lib)
-    assert o["accept_len"][0] == 0 and o["tokens"][0].tolist() == [2, -1]
+    """Cases worked by hand with dyadic probabilities (exact in binary),
+    stored with their derivations in tests/golden/closed_forms.json."""
+    for c in load_closed_forms():
+        o = svo.verify_stochastic(c["t"], c["d"], c["x"], c["ua"], c["us"], B=c["B"], k=c["k"],
+                                  V=c["V"], temperature=c["tau"], force=c["force"], lib=lib)
+        check_closed_form(c, o["accept_len"], o["tokens"], o["px"], o["qx"])
 
 
 # ------------------------------------------------------------------ P-INV ----

@@ -495,3 +495,27 @@ def test_sample(case):
     print(rep.summary())
     assert rep.ok(), rep.summary()
     assert repg.ok(), repg.summary()
+
+
+# ------------------------------------------------------- golden fixtures ----
+
+def test_closed_forms_on_gpu():
+    """The hand-worked cases of tests/golden/closed_forms.json, through the
+    library (dyadic probabilities: the float32 path must give exactly the
+    hand-derived decisions, tokens and probabilities)."""
+    from tests.oracle_pins import check_closed_form, load_closed_forms
+    for c in load_closed_forms():
+        if c["oracle_only"]:
+            continue
+        print("golden case", c["name"], flush=True)
+        B, k = c["B"], c["k"]
+        tt, dt = dev(c["t"]), dev(c["d"])
+        dbg = torch.full((B, k, 2), -1.0, dtype=torch.float32, device=DEV)
+        a, tok = binding.sv_verify_stochastic(tt, dt, dev(c["x"]), dev(c["ua"]), dev(c["us"]),
+                                              c["tau"], dbg_px_qx=dbg)
+        a2, tok2 = binding.sv_verify_stochastic(tt, dt, dev(c["x"]), dev(c["ua"]), dev(c["us"]),
+                                                c["tau"])
+        torch.cuda.synchronize()
+        pq = dbg.cpu().numpy()
+        check_closed_form(c, a.cpu().numpy(), tok.cpu().numpy(), pq[..., 0], pq[..., 1])
+        check_closed_form(c, a2.cpu().numpy(), tok2.cpu().numpy())
