@@ -519,3 +519,52 @@ def test_closed_forms_on_gpu():
         pq = dbg.cpu().numpy()
         check_closed_form(c, a.cpu().numpy(), tok.cpu().numpy(), pq[..., 0], pq[..., 1])
         check_closed_form(c, a2.cpu().numpy(), tok2.cpu().numpy())
+
+
+# ----------------------------------- full sizes of the benchmark's other modes
+
+@pytest.mark.parametrize("index", [2, 3])
+def test_workload_ragged(index):
+    """The ragged batch bench.py times (k_b ~ U{1..k} of workload 2 or 3):
+    full read (unequal lengths: row-split layout), early exit and greedy."""
+    rb = W.ragged(W.make(index))
+    s = rb.spec
+    print(f"ragged workload {index}: total draft rows {int(rb.cu[-1])}", flush=True)
+    rep, a = run_ragged(rb.cu, rb.target, rb.draft, rb.draft_tokens, rb.u_accept, rb.u_sample,
+                        rb.k_max, s.tau, s.dtype)
+    print(rep.summary(), "mean accept", a.mean())
+    assert rep.ok(), rep.summary()
+
+
+def test_workload_sample():
+    """Plain sampling as bench.py times it: target row 0 of every sequence of
+    workload 2 (256 rows of 128256 bf16 logits)."""
+    batch = W.make(2)
+    rows, u = W.sample_rows(batch)
+    s = batch.spec
+    tt, th, rs = logits_to_device(rows, s.dtype)
+    y = binding.sv_sample(tt, dev(u), s.tau)
+    yg = binding.sv_sample(tt, None, greedy=True)
+    torch.cuda.synchronize()
+    rep = protocol.compare_sample(th, u, B=s.B, V=s.V, temperature=s.tau,
+                                  tokens=y.cpu().numpy(), row_stride=rs)
+    repg = protocol.compare_sample(th, None, B=s.B, V=s.V, temperature=s.tau,
+                                   tokens=yg.cpu().numpy(), greedy=True, row_stride=rs)
+    print(rep.summary())
+    assert rep.ok(), rep.summary()
+    assert repg.ok(), repg.summary()
+
+
+def test_tree_batch_full():
+    """The draft-tree batch bench.py times: B=32 fixed 64-node trees,
+    V=128256 bf16 (exact)."""
+    tb = W.tree_batch()
+    B, N, V = tb.target.shape
+    tt, th, rs = logits_to_device(tb.target, tb.dtype)
+    a, tok, path = binding.sv_verify_greedy_tree(tt, dev(tb.node_tokens), dev(tb.parents))
+    torch.cuda.synchronize()
+    o = svo.verify_greedy_tree(th, tb.node_tokens, tb.parents, B=B, N=N, V=V, row_stride=rs)
+    assert np.array_equal(a.cpu().numpy(), o["accept_len"])
+    assert np.array_equal(tok.cpu().numpy(), o["tokens"])
+    assert np.array_equal(path.cpu().numpy(), o["path"])
+    print("mean accepted depth", o["accept_len"].mean())
