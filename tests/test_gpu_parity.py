@@ -568,3 +568,39 @@ def test_tree_batch_full():
     assert np.array_equal(tok.cpu().numpy(), o["tokens"])
     assert np.array_equal(path.cpu().numpy(), o["path"])
     print("mean accepted depth", o["accept_len"].mean())
+
+
+# ------------------------------------------------ vocabulary boundary sweep --
+
+BOUNDARY_V = [7, 8, 9, 15, 16, 17, 2047, 2048, 2049, 8191, 8192, 8193, 16383, 16384, 16385,
+              32767, 32768, 32769, 131071, 131072, 131073]
+
+
+@pytest.mark.parametrize("V", BOUNDARY_V)
+def test_vocabulary_boundaries(V):
+    """Vocabulary sizes just below, at and above the multiples the kernels cut
+    rows by (16-byte chunks of 8 bf16 / 4 f32, rounds of 256 and 1024 chunks,
+    slices of 4096 logits): stochastic (both layouts, with and without
+    diagnostics), greedy, sampling and a small tree, bf16 and f32, aligned and
+    unaligned rows."""
+    rng = np.random.default_rng(V)
+    for dtype, unal in ((W.BF16, False), (W.F32, True)):
+        for B in ((3, 192) if V <= 16385 else (3,)):
+            k = 2
+            print(f"V={V} dtype={dtype} unaligned={unal} B={B}", flush=True)
+            t, d, x, ua, us = make_stochastic(int(rng.integers(1 << 30)), B, k, V, dtype, 1.0)
+            rep, _, _ = run_stochastic(t, d, x, ua, us, 1.0, dtype, 0, unal)
+            assert rep.ok(), (V, dtype, B, rep.summary())
+            tg, xg = make_greedy(int(rng.integers(1 << 30)), B, 1, k, V, dtype, ties=True)
+            rep, _ = run_greedy(tg, xg, dtype, 0, unal)
+            assert rep.ok(), (V, dtype, B, rep.summary())
+        rows = W.round_logits(rng.standard_normal((5, V)) * 3, dtype)
+        u = W.exact_uniforms(rng, 5)
+        tt, th, rs = logits_to_device(rows, dtype, 0, unal)
+        y = binding.sv_sample(tt, dev(u), 1.0)
+        yg = binding.sv_sample(tt, None, greedy=True)
+        torch.cuda.synchronize()
+        assert protocol.compare_sample(th, u, B=5, V=V, temperature=1.0, tokens=y.cpu().numpy(),
+                                       row_stride=rs).ok()
+        assert protocol.compare_sample(th, None, B=5, V=V, temperature=1.0,
+                                       tokens=yg.cpu().numpy(), greedy=True, row_stride=rs).ok()
