@@ -91,16 +91,26 @@ def commit_bytes(accept, W: int) -> int:
     return 4 * B + 4 * B * W + 4 * B + 4 * int(sum(int(a) + 1 for a in accept)) + 4 * B + 4 * B
 
 
+def sample_one_pass(B: int, V: int, elem_bytes: int) -> bool:
+    """The library's layout choice for sv_sample with u on contiguous rows:
+    one workgroup per row when B <= 256 and V <= 40960 + 352 B (at most 32
+    rounds of 1024 16-byte chunks), else sliced rows."""
+    chunks = V // (16 // elem_bytes)
+    return B <= 256 and (chunks + 1023) // 1024 <= 32 and V <= 40960 + 352 * B
+
+
 def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -> str:
     """The kernel that dominates a call, following the library's layout
     choice: one workgroup per sequence for large single-candidate batches
-    (not for plain sampling, nor for ragged batches of unequal lengths read
-    in full), else the row-statistics kernel."""
+    (not for ragged batches of unequal lengths read in full), one per row for
+    plain sampling where that is faster, else the row-statistics kernel."""
+    if mode == "sample" and not greedy:
+        from draft_token_verification_10_amd.workloads import BF16
+        es = 2 if spec.dtype == BF16 else 4
+        return "k_sample_seq" if sample_one_pass(spec.B, spec.V, es) else "k_row_stats"
     if spec.G == 1 and spec.B >= 192:
         if greedy or mode == "greedy":
             return "k_greedy_seq"
-        if mode == "sample":
-            return "k_row_stats"
         if not diagnostics:
             return "k_stochastic_seq_exit"
         return "k_stochastic_seq" if uniform else "k_row_stats"

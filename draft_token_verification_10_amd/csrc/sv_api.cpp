@@ -47,8 +47,9 @@ struct Plan {
 //   ROW_SPLIT  the caller forces the row-split layout (ragged batches of
 //              unequal lengths with diagnostics: every row is read, and one
 //              workgroup per sequence would wait on the longest sequence);
-//   SAMPLE     plain sampling: row-split with sliced rows (the draw reads one
-//              slice again instead of the whole row).
+//   SAMPLE     plain sampling: one pass per row (use_sample_seq()) or
+//              row-split with sliced rows (the draw reads one slice again
+//              instead of the whole row).
 enum PlanFlags { kPlanDefault = 0, kPlanRowSplit = 1, kPlanSample = 2 };
 
 int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dtype,
@@ -58,6 +59,7 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     bool vec = ((row_stride * es) % 16) == 0;
     for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
     pl->seq = flags == kPlanDefault && sv::use_seq_resident(B, G);
+    if (flags & kPlanSample) pl->seq = sv::use_sample_seq(B, V, vec ? V / (16 / es) : V);
     pl->slice_draw = false;
     pl->rows_per_seq = rows_per_seq;
     pl->vec = vec;

@@ -43,7 +43,7 @@ inline int plan_slices(long long rows, int V) {
     return (int)s;
 }
 
-// Plain sampling (no draft positions) always takes the row-split layout with
+// Plain sampling (no draft positions) otherwise takes the row-split layout with
 // rows cut into slices of at most about kSampleSliceElems logits: the
 // statistics kernel then leaves per-slice normalisers, from which the draw
 // picks the slice holding r * Z and reads only that slice again.  (The bonus
@@ -51,6 +51,24 @@ inline int plan_slices(long long rows, int V) {
 // re-reading a slice measured slower there than the tile sums spread over
 // SD groups.)
 constexpr int kSampleSliceElems = 16384;
+// Short rows, or a batch that fills the GPU with one row per CU, are sampled
+// instead in one pass by one workgroup per row, with no workspace.  A row
+// then streams through a single CU (about 6 us plus 0.08 ns per logit on
+// MI355X, whatever the batch), while slicing spreads it over many; measured
+// over B in 1..512 and V in 32000..256000, one pass is the faster layout when
+// V <= kSampleSeqBaseElems + kSampleSeqElemsPerRow * B and B is at most the
+// 256 CUs (a second wave of rows doubles its time).  Its per-round partial
+// sums sit in registers, which caps a row at kSampleSeqRounds rounds of 1024
+// chunks.
+constexpr int kSampleSeqRounds = 32;
+constexpr int kSampleSeqMaxB = 256;
+constexpr long long kSampleSeqBaseElems = 40960;
+constexpr long long kSampleSeqElemsPerRow = 352;
+
+inline bool use_sample_seq(int B, int V, int chunks) {
+    return B <= kSampleSeqMaxB && (chunks + 1023) / 1024 <= kSampleSeqRounds &&
+           V <= kSampleSeqBaseElems + kSampleSeqElemsPerRow * B;
+}
 
 inline int plan_slices_sample(long long rows, int V) {
     int s = plan_slices(rows, V);

@@ -1338,6 +1338,112 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     if (threadIdx.x == 0) p.tokens_out[(size_t)b * (p.k + 1) + a] = y;
 }
 
+// Plain sampling in one pass, one row per 1024-thread workgroup: while the
+// row streams, every thread keeps -- besides its running normaliser -- the
+// sum it added in each round of NT chunks (relative to its current
+// reference, rescaled with it), so the per-round sums the inverse CDF scans
+// come from registers instead of a second pass over the row; only the round
+// holding the draw is read again.  Rows of at most SAMPLE_ROUNDS rounds.
+constexpr int SAMPLE_ROUNDS = kSampleSeqRounds;
+constexpr int SAMPLE_UNROLL = 4;  // rounds loaded per step (SAMPLE_ROUNDS a multiple)
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_SEQ) void k_sample_seq(Params p) {
+    using C = Chunk<DT, VEC>;
+    constexpr int NT = NT_SEQ;
+    constexpr int NW = NT / 64;
+    constexpr int E = C::E;
+    __shared__ StochFin<NT> sm;
+    __shared__ float wref[NW];
+    const int b = blockIdx.x;
+    const Seq sq = seq_of(p, b);
+    const int V = p.V;
+    const float c = p.c;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Row<DT, VEC> row(stoch_row<DT>(p, sq, 0), V);
+    const TileGeom g = tile_geom<NT>(row.nch, VEC ? V - row.nch * E : 0);
+    float rs[SAMPLE_ROUNDS];  // this thread's sum in each round
+    SoftAcc acc;
+#pragma unroll
+    for (int q = 0; q < SAMPLE_ROUNDS / SAMPLE_UNROLL; ++q) {
+        if (q * SAMPLE_UNROLL < g.rounds) {  // uniform
+            C buf[SAMPLE_UNROLL];
+#pragma unroll
+            for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+                const int ci = (q * SAMPLE_UNROLL + u) * NT + tid;
+                if (ci < g.nch) buf[u] = row.chunk(ci);
+                else buf[u].set_neg_inf();
+            }
+            float gm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < SAMPLE_UNROLL; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) gm = fmaxf(gm, buf[u].get(e));
+            const float gmc = gm * c;
+            if (gmc > acc.ref + RESCALE_MARGIN) {
+                const float f = fast_exp2(acc.ref - gmc);
+                acc.s0 *= f;
+#pragma unroll
+                for (int j = 0; j < q * SAMPLE_UNROLL; ++j) rs[j] *= f;
+                acc.ref = gmc;
+            }
+            const float nref = -acc.ref;
+#pragma unroll
+            for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+                float su = 0.0f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) su += fast_exp2(fmaf(buf[u].get(e), c, nref));
+                rs[q * SAMPLE_UNROLL + u] = su;
+                acc.s0 += su;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < SAMPLE_UNROLL; ++u) rs[q * SAMPLE_UNROLL + u] = 0.0f;
+        }
+    }
+    float trail = 0.0f;
+    if (tid < g.rem) {  // the row's last V mod E logits
+        const float x = row.elem(g.nch * E + tid);
+        if (x * c > acc.ref + RESCALE_MARGIN) {
+            const float f = fast_exp2(acc.ref - x * c);
+#pragma unroll
+            for (int j = 0; j < SAMPLE_ROUNDS; ++j) rs[j] *= f;
+            acc.ref = x * c;
+        }
+        trail = fast_exp2(fmaf(x, c, -acc.ref));
+    }
+    // the row's reference R (block max of the thread references)
+    const float wr = wave_max(acc.ref);
+    if (lane == 0) wref[wave] = wr;
+    for (int t = tid; t < g.nt_all * NW; t += NT) sm.tile_part[t] = 0.0f;
+    __syncthreads();
+    float R = wref[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) R = fmaxf(R, wref[w]);
+    const float f = fast_exp2(acc.ref - R);
+    // per-round sums relative to R: the inverse CDF's tiles (one round each)
+#pragma unroll
+    for (int j = 0; j < SAMPLE_ROUNDS; ++j) {
+        if (j < g.rounds) {  // uniform
+            const float w = wave_sum(rs[j] * f);
+            if (lane == 0) sm.tile_part[j * NW + wave] = w;
+        }
+    }
+    if (g.rem > 0) {
+        const float w = wave_sum(trail * f);
+        if (lane == 0) sm.tile_part[g.ntiles * NW + wave] = w;
+    }
+    __syncthreads();
+    const TargetW tw{c, -R};
+    float total;
+    const int y = cdf_select<DT, VEC, false, NT>(row, row, tw, p.u_sample[b], g, &total,
+                                                 sm.tile_part, sm.tile_excl, sm.sc);
+    if (tid == 0) {
+        p.tokens_out[b] = y;
+        if (p.accept_len) p.accept_len[b] = 0;
+    }
+}
+
 // Plain sampling after the statistics kernel (no decisions to take): one
 // workgroup per row draws from its slice statistics.
 constexpr int NT_SAMPLE = 512;
@@ -1521,6 +1627,8 @@ static int launch1(K kernel, const Params& p, long long grid, int block, void* s
 
 template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
+    if (seq && p.k == 0 && !p.cu)  // plain sampling in one pass
+        return launch1(k_sample_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
     if (seq)
         return p.dbg ? launch1(k_stochastic_seq<DT, VEC>, p, p.B, NT_SEQ, stream)
                      : launch1(k_stochastic_seq_exit<DT, VEC>, p, p.B, NT_SEQ, stream);

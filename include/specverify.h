@@ -65,7 +65,10 @@
  * 256-byte aligned.  Dense verification calls with k >= 1 need none when the
  * batch fills the GPU on its own (one candidate and B >= 192: every sequence
  * is then verified by a single workgroup), and accept NULL with size 0 there;
- * stochastic sampling calls (k = 0) always need it.  Its
+ * so does sv_sample with u when it samples each row in one pass (B <= 256
+ * and V <= 40960 + 352 B, the shapes where that is the faster layout).  Any
+ * other call given NULL returns SV_ERR_NULL, and one given too few or
+ * misaligned bytes SV_ERR_WORKSPACE, before launching anything.  Its
  * contents on entry do not matter and are unspecified on return.  Two calls
  * that overlap in time on the same workspace race.
  *

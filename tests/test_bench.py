@@ -80,6 +80,8 @@ def test_kernel_names_follow_layouts():
     assert bench.kernel_name(s2, "greedy") == "k_greedy_seq"
     assert bench.kernel_name(s2, "ragged", uniform=False) == "k_row_stats"
     assert bench.kernel_name(s2, "ragged", uniform=True) == "k_stochastic_seq"
-    assert bench.kernel_name(s2, "sample") == "k_row_stats"
+    assert bench.kernel_name(s2, "sample") == "k_sample_seq"
+    assert bench.kernel_name(s1, "sample") == "k_row_stats"
+    assert bench.kernel_name(s1, "sample", greedy=True) == "k_row_stats"
     assert bench.kernel_name(s2, "sample", greedy=True) == "k_greedy_seq"
     assert bench.kernel_name(s1, "stochastic") == "k_row_stats"

@@ -82,8 +82,8 @@ def test_workspace_bytes(lib):
     for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, -1, 10), (1, 1, 1, 0), (1, 1, 65, 10),
                  (1, 600, 1, 10)]:
         assert f(*args) == 0
-    # k = 0 (plain sampling) is a valid shape; sampling always cuts rows into
-    # slices of at most about 16384 logits (8 for V = 128256)
+    # k = 0 (plain sampling) is a valid shape; the bound covers the sliced
+    # layout's slices of at most about 16384 logits (8 for V = 128256)
     assert f(10, 1, 0, 1000) > 0
     assert f(256, 1, 0, 128256) >= 256 * 8 * 8
     # row-split: at least 8 bytes per row of every sequence
@@ -251,6 +251,11 @@ def test_sample_checks(lib):
     assert sample(lib, dtype=9) == SV_ERR_DTYPE
     assert sample(lib, V=0) == SV_ERR_SHAPE
     assert sample(lib, B=0, t=None, u=None, tok=None, ws=None, wsb=0) == SV_OK
+    # the sliced layout (more rows than the 256 CUs, or rows too long for
+    # one pass) needs the workspace: checked before any launch
+    assert sample(lib, B=300, ws=None, wsb=0) == SV_ERR_NULL
+    assert sample(lib, B=300, wsb=64) == SV_ERR_WORKSPACE
+    assert sample(lib, V=100000, rs=100000, ws=None, wsb=0) == SV_ERR_NULL
 
 
 def tree(lib, **kw):

@@ -8,6 +8,8 @@ unaligned rows (element-wise load path), -inf logits, out-of-vocabulary
 draft tokens and argmax ties; the five full workloads run at their real
 sizes in the same launch configuration the benchmark times.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -466,6 +468,13 @@ SAMPLE_CASES = [
     (3, 600000, W.BF16, 1.3, 0, False, None),
     (200, 1000, W.BF16, 1.0, 0, False, "ties"),
     (300, 32000, W.F32, 0.8, 0, True, None),
+    # either side of the one-pass layout's bounds (B <= 256 rows, V <= 40960
+    # + 352 B logits, 32 rounds of 1024 chunks)
+    (256, 131072, W.F32, 1.0, 0, False, None),
+    (256, 131080, W.BF16, 1.0, 0, False, None),
+    (257, 2048, W.BF16, 0.9, 0, False, None),
+    (64, 63488, W.BF16, 1.0, 0, False, None),
+    (64, 63496, W.BF16, 1.0, 0, False, None),
 ]
 
 
@@ -495,6 +504,34 @@ def test_sample(case):
     print(rep.summary())
     assert rep.ok(), rep.summary()
     assert repg.ok(), repg.summary()
+
+
+def test_sample_one_pass_without_workspace():
+    """Where rows are sampled in one pass, sv_sample takes a NULL workspace
+    and returns the tokens of the same call given one; where they are sliced
+    it refuses NULL before launching."""
+    lib = binding.load()
+    rng = np.random.default_rng(77)
+    for B, V, ok in ((32, 32000, True), (200, 128256, False)):
+        print(f"sample without workspace B={B} V={V}", flush=True)
+        t = W.round_logits(rng.standard_normal((B, V)) * 3, W.BF16)
+        u = W.exact_uniforms(rng, B)
+        tt, th, rs = logits_to_device(t, W.BF16, 0, False)
+        ud = dev(u)
+        y = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+        s = torch.cuda.current_stream().cuda_stream
+        st = lib.sv_sample(ctypes.c_void_p(tt.data_ptr()), ctypes.c_void_p(ud.data_ptr()), B, V,
+                           rs, binding.SV_DTYPE_BF16, 1.0, 0, ctypes.c_void_p(y.data_ptr()),
+                           None, 0, ctypes.c_void_p(s))
+        if not ok:
+            assert st == -1 and bool((y == -7).all())
+            continue
+        assert st == 0, lib.sv_status_string(st)
+        want = binding.sv_sample(tt, ud, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(y, want)
+        assert protocol.compare_sample(th, u, B=B, V=V, temperature=1.0, tokens=y.cpu().numpy(),
+                                       row_stride=rs).ok()
 
 
 # ------------------------------------------------------- golden fixtures ----
