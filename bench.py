@@ -24,6 +24,10 @@ Modes:
   commit      sv_commit of the workload's verified step (B sequences, k+1
               token slots): a launch-bound kernel, timed on its own
 
+Every HBM-bound line also carries "achievable_read": the rate of a plain
+read with the same loads (sv_stream_read over 2 GiB) and the path's fraction
+of it, beside the fraction of the 8 TB/s peak.
+
 Inputs smaller than 512 MB are replicated and the copies rotated from call to
 call, so that no call finds its logits in the 256 MB last-level cache (cold
 figures); "warm" repeats the timing on one copy.
@@ -240,6 +244,27 @@ def cpu_baseline(run, B: int, what: str, min_reps: int = 3, target_s: float = 10
                       f"({sum(times):.1f} s), median pass {med:.3f} s"}
 
 
+def achievable_read(torch, binding, dev, achieved_gbs: float, nbytes: int = 2 << 30,
+                    steps: int = 20) -> dict:
+    """The read rate a plain stream with the logit kernels' own loads sustains
+    (sv_stream_read: every byte of a 2 GiB buffer, eight times the last-level
+    cache, read once by N workgroups each taking one contiguous share), for
+    several N; the best is the practical ceiling reported beside the peak."""
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    sweep = {}
+    for blocks in (256, 512, 1024, 2048, 4096):
+        ms, _ = time_calls([lambda b=blocks: binding.sv_stream_read(buf, b, out)], steps, 3,
+                           torch)
+        sweep[str(blocks)] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    best = max(sweep, key=sweep.get)
+    del buf
+    return {"GBps": sweep[best], "frac_of_peak": round(sweep[best] / HBM_PEAK_GBS, 4),
+            "workgroups": int(best), "bytes": nbytes, "kernel": "k_stream_read",
+            "GBps_by_workgroups": sweep,
+            "path_frac_of_achievable": round(achieved_gbs / sweep[best], 4)}
+
+
 def line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_config=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     cfg = {"workload": spec.name, "B": spec.B, "k": spec.k, "V": spec.V, "G": spec.G,
@@ -319,6 +344,7 @@ def bench_tree(args, torch, dev, binding, workloads):
         "per_call_us": per_call_us(fns, min(args.steps, 100), torch),
         "mean_accepted_depth": round(float(acc.float().mean().item()), 4),
     }
+    result["achievable_read"] = achievable_read(torch, binding, dev, gbs)
     if not args.no_cpu_baseline:
         from oracle import svo
         result["cpu_baseline"] = cpu_baseline(
@@ -535,6 +561,7 @@ def main():
         sides["greedy"] = side(spec, fns_g, gb, kernel_name(spec, mode, greedy=True),
                                f"{traffic_key}_greedy", args, torch)
     result.update(sides)
+    result["achievable_read"] = achievable_read(torch, binding, dev, result["achieved_GBps"])
 
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)

@@ -55,6 +55,8 @@ def load(path: str | None = None):
     lib.sv_workspace_bytes.restype = SZ
     lib.sv_status_string.argtypes = [I]
     lib.sv_status_string.restype = ctypes.c_char_p
+    lib.sv_stream_read.argtypes = [P, SZ, I, P, P]
+    lib.sv_stream_read.restype = I
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -406,3 +408,19 @@ def sv_commit(accept_len: torch.Tensor, tokens: torch.Tensor, seq_len: torch.Ten
     if st != SV_OK:
         raise SpecVerifyError(st)
     return seq_len, history, next_token
+
+
+def sv_stream_read(buf: torch.Tensor, blocks: int, out: torch.Tensor, stream=None) -> None:
+    """Measurement aid: read the contiguous device tensor `buf` once with the
+    logit stream's loads, `blocks` workgroups each reading one contiguous
+    share; `out` (int32 [1] on the same device) is XORed with a checksum."""
+    _dev(buf)
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if out.dtype != torch.int32 or out.numel() < 1 or out.device != buf.device:
+        raise ValueError("out must be an int32 tensor on buf's device")
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device).cuda_stream
+    st = load().sv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(blocks),
+                               _ptr(out), ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include "specverify.h"
+#include "sv_measure.h"
 
 int main(void) {
     int fails = 0;
@@ -23,6 +24,8 @@ int main(void) {
         SV_ERR_TEMPERATURE)
         ++fails;
     if (sv_commit(NULL, NULL, 0, 1, NULL, NULL, 0, 0, NULL, 1, NULL) != SV_OK) ++fails;
+    if (sv_stream_read(NULL, 0, 1, NULL, NULL) != SV_OK) ++fails;
+    if (sv_stream_read(dummy, 15, 1, (uint32_t*)dummy, NULL) != SV_ERR_SHAPE) ++fails;
     if (sv_workspace_bytes(64, 1, 4, 128256) == 0) ++fails;
     if (sv_status_string(SV_ERR_WORKSPACE)[0] == '\0') ++fails;
     printf("%s\n", fails ? "FAIL" : "ok");

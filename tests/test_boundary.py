@@ -15,10 +15,15 @@ SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_TEMPERATURE, SV_ERR_WORKS
     0, -1, -2, -3, -4, -5, -6
 
 
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+
+
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(sv_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def header_constants():
@@ -36,9 +41,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["sv_commit", "sv_sample", "sv_status_string", "sv_verify_greedy",
-                     "sv_verify_greedy_ragged", "sv_verify_greedy_tree", "sv_verify_stochastic",
-                     "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
+    assert names == ["sv_commit", "sv_sample", "sv_status_string", "sv_stream_read",
+                     "sv_verify_greedy", "sv_verify_greedy_ragged", "sv_verify_greedy_tree",
+                     "sv_verify_stochastic", "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -326,3 +331,15 @@ def test_header_is_plain_c_and_links(tmp_path):
                    check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.stdout, r.stderr)
+
+
+def test_stream_read_checks(lib):
+    out = ctypes.c_void_p(1 << 22)
+    assert lib.sv_stream_read(None, 0, 1, None, None) == SV_OK
+    assert lib.sv_stream_read(None, 16, 1, out, None) == SV_ERR_NULL
+    assert lib.sv_stream_read(A, 16, 1, None, None) == SV_ERR_NULL
+    assert lib.sv_stream_read(A, 24, 1, out, None) == SV_ERR_SHAPE
+    assert lib.sv_stream_read(ctypes.c_void_p((1 << 20) + 4), 16, 1, out, None) == SV_ERR_SHAPE
+    for blocks in (0, -1, 65537):
+        assert lib.sv_stream_read(A, 16, blocks, out, None) == SV_ERR_SHAPE
+    assert lib.sv_stream_read(A, 1 << 32, 1, out, None) == SV_ERR_SHAPE  # share above 2 GiB
