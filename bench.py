@@ -251,7 +251,7 @@ def achievable_read(torch, binding, dev, achieved_gbs: float, nbytes: int = 2 <<
     cache, read once by N workgroups each taking one contiguous share), for
     several N; the best is the practical ceiling reported beside the peak."""
     buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.zeros(4096, dtype=torch.int32, device=dev)
     sweep = {}
     for blocks in (256, 512, 1024, 2048, 4096):
         ms, _ = time_calls([lambda b=blocks: binding.sv_stream_read(buf, b, out)], steps, 3,

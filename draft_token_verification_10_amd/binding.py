@@ -413,12 +413,13 @@ def sv_commit(accept_len: torch.Tensor, tokens: torch.Tensor, seq_len: torch.Ten
 def sv_stream_read(buf: torch.Tensor, blocks: int, out: torch.Tensor, stream=None) -> None:
     """Measurement aid: read the contiguous device tensor `buf` once with the
     logit stream's loads, `blocks` workgroups each reading one contiguous
-    share; `out` (int32 [1] on the same device) is XORed with a checksum."""
+    share; `out` (int32 [>= blocks] on the same device) receives one XOR
+    checksum per workgroup."""
     _dev(buf)
     if not buf.is_contiguous():
         raise ValueError("buf must be contiguous")
-    if out.dtype != torch.int32 or out.numel() < 1 or out.device != buf.device:
-        raise ValueError("out must be an int32 tensor on buf's device")
+    if out.dtype != torch.int32 or out.numel() < blocks or out.device != buf.device:
+        raise ValueError("out must be an int32 tensor of at least `blocks` words on buf's device")
     s = stream if stream is not None else torch.cuda.current_stream(buf.device).cuda_stream
     st = load().sv_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(blocks),
                                _ptr(out), ctypes.c_void_p(s))

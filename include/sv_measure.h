@@ -25,8 +25,10 @@ extern "C" {
  *            of `blocks` equal contiguous shares, as a sequence-resident
  *            verification workgroup reads its sequence's rows (each share at
  *            most 2 GiB)
- *   out      device uint32: XORed with a checksum of the bytes read, so that
- *            the loads are kept (its value carries no other meaning)
+ *   out      device uint32 [blocks]: word i receives the XOR of the 32-bit
+ *            words of workgroup i's share (so that the loads are kept); words
+ *            of workgroups left without a share (more blocks than 16-byte
+ *            chunks) are not written
  * Asynchronous; returns SV_OK, SV_ERR_NULL (src or out NULL, bytes > 0),
  * SV_ERR_SHAPE (misaligned src, bytes not a multiple of 16, blocks out of
  * range, a share above 2 GiB) or SV_ERR_HIP (launch refused), checked on the
