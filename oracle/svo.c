@@ -476,3 +476,12 @@ int svo_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads for the following calls (timing only; results do not depend on it). */
+void svo_set_num_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

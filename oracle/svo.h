@@ -153,6 +153,7 @@ int svo_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
 
 /* Number of OpenMP threads the batched entry points use. */
 int svo_num_threads(void);
+void svo_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

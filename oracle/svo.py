@@ -61,6 +61,8 @@ def _bind(lib):
     lib.svo_commit.restype = I
     lib.svo_num_threads.argtypes = []
     lib.svo_num_threads.restype = I
+    lib.svo_set_num_threads.argtypes = [I]
+    lib.svo_set_num_threads.restype = None
     return lib
 
 
@@ -270,3 +272,8 @@ def commit(accept_len, tokens, seq_len, history, *, capacity=None, next_stride=1
 
 def num_threads(lib=None) -> int:
     return (lib or load()).svo_num_threads()
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing only)."""
+    (lib or load()).svo_set_num_threads(int(n))

@@ -85,3 +85,20 @@ def test_kernel_names_follow_layouts():
     assert bench.kernel_name(s1, "sample", greedy=True) == "k_row_stats"
     assert bench.kernel_name(s2, "sample", greedy=True) == "k_greedy_seq"
     assert bench.kernel_name(s1, "stochastic") == "k_row_stats"
+
+
+def test_cpu_baseline_reports_threads_and_single_thread():
+    """The oracle timing leg: the threaded figure, a one-thread pass beside
+    it, and the oracle's thread count restored afterwards."""
+    import numpy as np
+    from oracle import svo
+    rng = np.random.default_rng(3)
+    rows = rng.standard_normal((4, 1000)).astype(np.float32)
+    u = np.full(4, 0.5, np.float32)
+    before = svo.num_threads()
+    out = bench.cpu_baseline(lambda: svo.sample(rows, u, B=4, V=1000), 4, "a tiny batch",
+                             min_reps=3, target_s=0.05)
+    assert svo.num_threads() == before
+    assert out["kind"] == "oracle" and out["cores"] == before and out["value"] > 0
+    st = out["single_thread"]
+    assert st["cores"] == 1 and st["value"] > 0 and st["unit"] == "seqs/s"
