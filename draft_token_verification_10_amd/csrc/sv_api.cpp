@@ -114,9 +114,9 @@ extern "C" {
 size_t sv_workspace_bytes(int B, int G, int k, int V) {
     if (check_shape(B, G, k, V, V) != SV_OK) return 0;
     // Enough for every entry point at any B: the stochastic ones (one
-    // candidate) may take the row-split layout (sampling always does, ragged
-    // batches with diagnostics may), and so do greedy calls below the
-    // sequence-resident threshold and tree verification (G = N nodes, k = 0).
+    // candidate) may take the row-split layout (sampling outside the one-pass
+    // shapes, ragged batches with diagnostics), and so do greedy calls below
+    // the sequence-resident threshold and tree verification (G = N, k = 0).
     const size_t s = rowsplit_need(B, 2 * k + 1, V, true, k == 0);
     const size_t g = rowsplit_need(B, G * (k + 1), V, false, false);
     return s > g ? s : g;

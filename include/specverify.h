@@ -65,8 +65,8 @@
  * 256-byte aligned.  Dense verification calls with k >= 1 need none when the
  * batch fills the GPU on its own (one candidate and B >= 192: every sequence
  * is then verified by a single workgroup), and accept NULL with size 0 there;
- * so does sv_sample with u when it samples each row in one pass (B <= 256
- * and V <= 40960 + 352 B, the shapes where that is the faster layout).  Any
+ * so does sv_sample with u when it samples each row in one pass (see
+ * sv_sample).  Any
  * other call given NULL returns SV_ERR_NULL, and one given too few or
  * misaligned bytes SV_ERR_WORKSPACE, before launching anything.  Its
  * contents on entry do not matter and are unspecified on return.  Two calls
@@ -201,7 +201,10 @@ int sv_verify_greedy_ragged(const void* target_logits, const int32_t* draft_toke
  *            zero: inverse CDF of softmax(row / temperature) at u[b]
  *   tokens   out int32 [B]
  * It is the verification of sequences with no draft tokens.  Workspace:
- * sv_workspace_bytes(B, 1, 0, V).
+ * sv_workspace_bytes(B, 1, 0, V); none (NULL, 0) when not greedy, B <= 256
+ * and V <= 40960 + 352 B (and V <= 32768 unless logits and the row stride
+ * are 16-byte aligned), where each row is sampled in one pass by one
+ * workgroup (the faster layout there).
  */
 int sv_sample(const void* logits, const float* u, int B, int V, int64_t row_stride, int dtype,
               float temperature, int greedy, int32_t* tokens, void* workspace,
