@@ -33,6 +33,11 @@
 namespace sv {
 
 constexpr int NT_SEQ = 1024;   // sequence-resident workgroup: 16 wave64s
+// More sequences than CUs: 512-thread workgroups, two resident per CU, so the
+// whole batch streams at once instead of in rounds of one workgroup per CU
+// (B=512, k=3: 174 against 181 us; at B=256 the 1024-thread groups win).
+constexpr int NT_SEQ_WIDE = 512;
+constexpr int kSeqWideMinB = 257;
 constexpr int NT_ROW = 256;    // row-split statistics workgroup: 4 wave64s
 constexpr int NT_FIN = 1024;   // row-split finishing workgroup
 constexpr int UNROLL = 4;      // 16-byte loads in flight per lane while streaming
@@ -845,16 +850,17 @@ __device__ __forceinline__ void merge_row(const float* wR, const float* wZ, int 
     for (int w = 0; w < NW; ++w) Z += wZ[r * NW + w] * fast_exp2(wR[r * NW + w] - R);
 }
 
+template <int NT>
 struct StochSeqSmem {
-    StochFin<NT_SEQ> fin;
-    float wR[MAX_ROWS_STOCH * (NT_SEQ / 64)];  // per-wave partial normalisers
-    float wZ[MAX_ROWS_STOCH * (NT_SEQ / 64)];
+    StochFin<NT> fin;
+    float wR[MAX_ROWS_STOCH * (NT / 64)];  // per-wave partial normalisers
+    float wZ[MAX_ROWS_STOCH * (NT / 64)];
 };
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
-    constexpr int NW = NT_SEQ / 64;
-    __shared__ StochSeqSmem sm;
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_stochastic_seq(Params p) {
+    constexpr int NW = NT / 64;
+    __shared__ StochSeqSmem<NT> sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Seq sq = seq_of(p, b);
@@ -868,8 +874,8 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
         const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
         const Row<DT, VEC> row(stoch_row<DT>(p, sq, r), p.V);
         SoftAcc acc;
-        if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT_SEQ, true>(row, p.c, acc);
-        else stream_softmax<DT, VEC, NT_SEQ>(row, p.c, acc);
+        if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT, true>(row, p.c, acc);
+        else stream_softmax<DT, VEC, NT>(row, p.c, acc);
         float R, Z;
         wave_softmax(acc, R, Z);
         if (lane == 0) {
@@ -878,7 +884,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
         }
     }
     __syncthreads();
-    for (int r = tid; r < rows; r += NT_SEQ) {
+    for (int r = tid; r < rows; r += NT) {
         float R = sm.wR[r * NW];
 #pragma unroll
         for (int w = 1; w < NW; ++w) R = fmaxf(R, sm.wR[r * NW + w]);
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
         sm.fin.Z[r] = Z;
     }
     __syncthreads();
-    finish_stochastic<DT, VEC, NT_SEQ>(p, b, sq, sm.fin);
+    finish_stochastic<DT, VEC, NT>(p, b, sq, sm.fin);
 }
 
 // Early-exit variant, used when no per-position diagnostics are asked for:
@@ -897,21 +903,21 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq(Params p) {
 // rejection, because no later row can change accept_len or tokens.  One
 // block-wide decision per position: after pair i every thread merges the
 // pair's per-wave partials from LDS and reaches the same verdict.
+template <int NT>
 struct StochExitSmem {
-    StochFin<NT_SEQ> fin;
-    float wR[2 * 2 * (NT_SEQ / 64)];  // [pair parity][target, draft][wave]
-    float wZ[2 * 2 * (NT_SEQ / 64)];
+    StochFin<NT> fin;
+    float wR[2 * 2 * (NT / 64)];  // [pair parity][target, draft][wave]
+    float wZ[2 * 2 * (NT / 64)];
     int xv[kMaxK];    // draft tokens
     float uv[kMaxK];  // acceptance uniforms
     float tv[kMaxK];  // target logit at the draft token (0 if out of range)
     float dv[kMaxK];  // draft logit at the draft token
 };
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
-    constexpr int NT = NT_SEQ;
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     constexpr int NW = NT / 64;
-    __shared__ StochExitSmem sm;
+    __shared__ StochExitSmem<NT> sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Seq sq = seq_of(p, b);
@@ -1015,16 +1021,17 @@ __global__ __launch_bounds__(NT_SEQ) void k_stochastic_seq_exit(Params p) {
     }
 }
 
+template <int NT>
 struct GreedySeqSmem {
-    GreedyFin<NT_SEQ> fin;
-    float wbest[MAX_ROWS_GREEDY_SEQ * (NT_SEQ / 64)];
-    int wpos[MAX_ROWS_GREEDY_SEQ * (NT_SEQ / 64)];
+    GreedyFin<NT> fin;
+    float wbest[MAX_ROWS_GREEDY_SEQ * (NT / 64)];
+    int wpos[MAX_ROWS_GREEDY_SEQ * (NT / 64)];
 };
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
-    constexpr int NW = NT_SEQ / 64;
-    __shared__ GreedySeqSmem sm;
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_greedy_seq(Params p) {
+    constexpr int NW = NT / 64;
+    __shared__ GreedySeqSmem<NT> sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Seq sq = seq_of(p, b);
@@ -1032,7 +1039,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
     for (int r = 0; r < rows; ++r) {
         const Row<DT, VEC> row(greedy_row<DT>(p, sq, r), p.V);
         ArgAcc acc;
-        stream_argmax<DT, VEC, NT_SEQ>(row, acc);
+        stream_argmax<DT, VEC, NT>(row, acc);
         wave_argmax(acc.best, acc.pos);
         if (lane == 0) {
             sm.wbest[r * NW + wave] = acc.best;
@@ -1040,7 +1047,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
         }
     }
     __syncthreads();
-    for (int r = tid; r < rows; r += NT_SEQ) {
+    for (int r = tid; r < rows; r += NT) {
         float best = sm.wbest[r * NW];
         int pos = sm.wpos[r * NW];
         for (int w = 1; w < NW; ++w)
@@ -1052,7 +1059,7 @@ __global__ __launch_bounds__(NT_SEQ) void k_greedy_seq(Params p) {
         sm.fin.g[r] = argmax_refine(row, best, pos);
     }
     __syncthreads();
-    finish_greedy<NT_SEQ>(p, b, sq, sm.fin);
+    finish_greedy<NT>(p, b, sq, sm.fin);
 }
 
 // ------------------------------------------------------------------------
@@ -1629,9 +1636,13 @@ template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     if (seq && p.k == 0 && !p.cu)  // plain sampling in one pass
         return launch1(k_sample_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+    if (seq && p.B >= kSeqWideMinB)
+        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE,
+                               stream);
     if (seq)
-        return p.dbg ? launch1(k_stochastic_seq<DT, VEC>, p, p.B, NT_SEQ, stream)
-                     : launch1(k_stochastic_seq_exit<DT, VEC>, p, p.B, NT_SEQ, stream);
+        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
     const long long items = (long long)p.B * p.rows_per_seq * p.S;
     int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
     if (e) return e;
@@ -1643,7 +1654,9 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
 
 template <int DT, bool VEC>
 static int launch_greedy_t(const Params& p, bool seq, void* stream) {
-    if (seq) return launch1(k_greedy_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+    if (seq && p.B >= kSeqWideMinB)
+        return launch1(k_greedy_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
+    if (seq) return launch1(k_greedy_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
     const long long items = (long long)p.B * p.rows_per_seq * p.S;
     int e = launch1(k_row_stats<DT, VEC, false>, p, items, NT_ROW, stream);
     if (e) return e;

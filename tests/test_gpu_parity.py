@@ -151,6 +151,7 @@ STOCH_CASES = [
     # the maximum draft length, both layouts
     (3, 64, 1000, W.BF16, 1.0, 0, False, "close"),
     (192, 64, 300, W.F32, 1.0, 0, False, "close"),
+    (600, 64, 300, W.F32, 1.0, 0, True, "close"),  # more sequences than CUs
     # extreme temperatures (exponents far from 0 after scaling)
     (6, 4, 50000, W.BF16, 0.05, 0, False, None),
     (200, 3, 4103, W.F32, 20.0, 0, False, None),
@@ -212,6 +213,7 @@ GREEDY_CASES = [
     # the largest sequence: 16 candidates of 64 rows (1024 rows), and k = 64
     (2, 16, 63, 700, W.BF16, 0, False, True),
     (200, 1, 64, 500, W.F32, 0, True, True),
+    (520, 1, 64, 500, W.BF16, 0, False, True),  # more sequences than CUs
 ]
 
 
