@@ -97,10 +97,13 @@ def commit_bytes(accept, W: int) -> int:
 
 def sample_one_pass(B: int, V: int, elem_bytes: int) -> bool:
     """The library's layout choice for sv_sample with u on contiguous rows:
-    one workgroup per row when B <= 256 and V <= 40960 + 352 B (at most 32
-    rounds of 1024 16-byte chunks), else sliced rows."""
+    one workgroup per row (1024 threads up to 256 rows, 512 beyond) where
+    that is faster, else sliced rows."""
     chunks = V // (16 // elem_bytes)
-    return B <= 256 and (chunks + 1023) // 1024 <= 32 and V <= 40960 + 352 * B
+    if B > 256:
+        return (B <= 512 and (chunks + 511) // 512 <= 32 and
+                (V <= 40960 or (B >= 320 and V <= 98304)))
+    return (chunks + 1023) // 1024 <= 32 and V <= 40960 + 352 * B
 
 
 def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -> str:

@@ -24,6 +24,12 @@ constexpr int kMaxRowsPerSeq = 1024;
 //    The kernel boundary makes the statistics visible.  Used for small
 //    batches and for several candidates per sequence.
 constexpr int kSeqResidentMinB = 192;
+// Sequence-resident workgroup size: 1024 threads (one group per CU), or 512
+// threads once the sequences outnumber the 256 CUs, so that two or more share
+// a CU and the whole batch streams at once instead of in rounds.
+constexpr int kSeqThreads = 1024;
+constexpr int kSeqWideThreads = 512;
+constexpr int kSeqWideMinB = 257;
 
 inline bool use_seq_resident(int B, int G) { return G == 1 && B >= kSeqResidentMinB; }
 
@@ -54,19 +60,31 @@ constexpr int kSampleSliceElems = 16384;
 // Short rows, or a batch that fills the GPU with one row per CU, are sampled
 // instead in one pass by one workgroup per row, with no workspace.  A row
 // then streams through a single CU (about 6 us plus 0.08 ns per logit on
-// MI355X, whatever the batch), while slicing spreads it over many; measured
-// over B in 1..512 and V in 32000..256000, one pass is the faster layout when
-// V <= kSampleSeqBaseElems + kSampleSeqElemsPerRow * B and B is at most the
-// 256 CUs (a second wave of rows doubles its time).  Its per-round partial
-// sums sit in registers, which caps a row at kSampleSeqRounds rounds of 1024
-// chunks.
+// MI355X, whatever the batch), while slicing spreads it over many.  Measured
+// over B in 1..512 and V in 32000..256000 (bf16), one pass is the faster
+// layout
+//   * with 1024-thread groups, B < kSeqWideMinB: when V <= kSampleSeqBaseElems +
+//     kSampleSeqElemsPerRow * B (beyond the 256 CUs a second wave of rows
+//     doubles the time);
+//   * with 512-thread groups, two per CU, kSeqWideMinB <= B <= 512: when V <=
+//     kSampleSeqBaseElems, or B >= kSampleWideMidB and V <=
+//     kSampleWideMaxElems.
+// Its per-round partial sums sit in registers, which caps a row at
+// kSampleSeqRounds rounds of one chunk per thread.
 constexpr int kSampleSeqRounds = 32;
-constexpr int kSampleSeqMaxB = 256;
 constexpr long long kSampleSeqBaseElems = 40960;
 constexpr long long kSampleSeqElemsPerRow = 352;
+constexpr int kSampleWideMaxB = 512;
+constexpr int kSampleWideMidB = 320;
+constexpr long long kSampleWideMaxElems = 98304;
 
 inline bool use_sample_seq(int B, int V, int chunks) {
-    return B <= kSampleSeqMaxB && (chunks + 1023) / 1024 <= kSampleSeqRounds &&
+    if (B >= kSeqWideMinB) {  // kSeqWideThreads-thread groups
+        return B <= kSampleWideMaxB &&
+               (chunks + kSeqWideThreads - 1) / kSeqWideThreads <= kSampleSeqRounds &&
+               (V <= kSampleSeqBaseElems || (B >= kSampleWideMidB && V <= kSampleWideMaxElems));
+    }
+    return (chunks + kSeqThreads - 1) / kSeqThreads <= kSampleSeqRounds &&
            V <= kSampleSeqBaseElems + kSampleSeqElemsPerRow * B;
 }
 

@@ -32,12 +32,11 @@
 
 namespace sv {
 
-constexpr int NT_SEQ = 1024;   // sequence-resident workgroup: 16 wave64s
-// More sequences than CUs: 512-thread workgroups, two resident per CU, so the
-// whole batch streams at once instead of in rounds of one workgroup per CU
-// (B=512, k=3: 174 against 181 us; at B=256 the 1024-thread groups win).
-constexpr int NT_SEQ_WIDE = 512;
-constexpr int kSeqWideMinB = 257;
+constexpr int NT_SEQ = kSeqThreads;  // sequence-resident workgroup: 16 wave64s
+// More sequences than CUs (B >= kSeqWideMinB): 512-thread workgroups, two or
+// more resident per CU (B=512, k=3: 174 against 181 us; at B=256 the
+// 1024-thread groups win).
+constexpr int NT_SEQ_WIDE = kSeqWideThreads;
 constexpr int NT_ROW = 256;    // row-split statistics workgroup: 4 wave64s
 constexpr int NT_FIN = 1024;   // row-split finishing workgroup
 constexpr int UNROLL = 4;      // 16-byte loads in flight per lane while streaming
@@ -1354,10 +1353,9 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
 constexpr int SAMPLE_ROUNDS = kSampleSeqRounds;
 constexpr int SAMPLE_UNROLL = 4;  // rounds loaded per step (SAMPLE_ROUNDS a multiple)
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_SEQ) void k_sample_seq(Params p) {
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
     using C = Chunk<DT, VEC>;
-    constexpr int NT = NT_SEQ;
     constexpr int NW = NT / 64;
     constexpr int E = C::E;
     __shared__ StochFin<NT> sm;
@@ -1635,7 +1633,9 @@ static int launch1(K kernel, const Params& p, long long grid, int block, void* s
 template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     if (seq && p.k == 0 && !p.cu)  // plain sampling in one pass
-        return launch1(k_sample_seq<DT, VEC>, p, p.B, NT_SEQ, stream);
+        return p.B >= kSeqWideMinB
+                   ? launch1(k_sample_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
+                   : launch1(k_sample_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
     if (seq && p.B >= kSeqWideMinB)
         return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
                      : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE,

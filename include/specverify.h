@@ -201,10 +201,11 @@ int sv_verify_greedy_ragged(const void* target_logits, const int32_t* draft_toke
  *            zero: inverse CDF of softmax(row / temperature) at u[b]
  *   tokens   out int32 [B]
  * It is the verification of sequences with no draft tokens.  Workspace:
- * sv_workspace_bytes(B, 1, 0, V); none (NULL, 0) when not greedy, B <= 256
- * and V <= 40960 + 352 B (and V <= 32768 unless logits and the row stride
- * are 16-byte aligned), where each row is sampled in one pass by one
- * workgroup (the faster layout there).
+ * sv_workspace_bytes(B, 1, 0, V); none (NULL, 0) where each row is sampled
+ * in one pass by one workgroup (the faster layout there): not greedy, and
+ * B <= 256 with V <= 40960 + 352 B, or 256 < B <= 512 with V <= 40960 or
+ * (B >= 320 and) V <= 98304 -- with V at most 32768 (B <= 256) or 16384
+ * (B > 256) unless logits and the row stride are 16-byte aligned.
  */
 int sv_sample(const void* logits, const float* u, int B, int V, int64_t row_stride, int dtype,
               float temperature, int greedy, int32_t* tokens, void* workspace,

@@ -82,6 +82,8 @@ def test_kernel_names_follow_layouts():
     assert bench.kernel_name(s2, "ragged", uniform=True) == "k_stochastic_seq"
     assert bench.kernel_name(s2, "sample") == "k_sample_seq"
     assert bench.kernel_name(s1, "sample") == "k_row_stats"
+    assert bench.sample_one_pass(512, 98304, 2) and not bench.sample_one_pass(512, 128256, 2)
+    assert bench.sample_one_pass(257, 32000, 2) and not bench.sample_one_pass(300, 65536, 2)
     assert bench.kernel_name(s1, "sample", greedy=True) == "k_row_stats"
     assert bench.kernel_name(s2, "sample", greedy=True) == "k_greedy_seq"
     assert bench.kernel_name(s1, "stochastic") == "k_row_stats"

@@ -477,6 +477,13 @@ SAMPLE_CASES = [
     (257, 2048, W.BF16, 0.9, 0, False, None),
     (64, 63488, W.BF16, 1.0, 0, False, None),
     (64, 63496, W.BF16, 1.0, 0, False, None),
+    # more rows than CUs: one pass with 512-thread groups, or sliced rows
+    (300, 40960, W.BF16, 1.0, 0, False, None),
+    (320, 98304, W.BF16, 0.8, 0, False, None),
+    (512, 65536, W.F32, 1.0, 0, False, None),
+    (300, 65536, W.BF16, 1.0, 0, False, None),
+    (512, 98312, W.BF16, 1.0, 0, False, None),
+    (400, 16384, W.F32, 1.0, 1, True, "neginf"),
 ]
 
 
