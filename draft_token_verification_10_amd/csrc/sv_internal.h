@@ -30,6 +30,10 @@ constexpr int kSeqResidentMinB = 192;
 constexpr int kSeqThreads = 1024;
 constexpr int kSeqWideThreads = 512;
 constexpr int kSeqWideMinB = 257;
+// Row-split stochastic calls with at least this many sequences (one per CU)
+// finish each sequence in one 1024-thread workgroup; smaller batches spread
+// the closing-token draw over SD workgroups per sequence instead.
+constexpr int kFinishOneGroupMinB = 256;
 
 inline bool use_seq_resident(int B, int G) { return G == 1 && B >= kSeqResidentMinB; }
 

@@ -1133,6 +1133,30 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
     }
 }
 
+// Row-split stochastic finish for batches that fill the GPU on their own:
+// one 1024-thread workgroup per sequence merges the slice statistics, takes
+// the decisions and draws the closing token, as the sequence-resident kernel
+// finishes -- one launch instead of the two below.
+template <int DT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void k_stochastic_finish(Params p) {
+    __shared__ StochFin<NT> sm;
+    const int b = blockIdx.x;
+    const Seq sq = seq_of(p, b);
+    const int rows = 2 * sq.k + 1, S = p.S;
+    const float* part = p.part + (size_t)b * p.rows_per_seq * S * 2;
+    for (int r = threadIdx.x; r < rows; r += NT) {
+        float R = -FLT_MAX;
+        for (int j = 0; j < S; ++j) R = fmaxf(R, part[(r * S + j) * 2]);
+        float Z = 0.0f;
+        for (int j = 0; j < S; ++j)
+            Z += part[(r * S + j) * 2 + 1] * fast_exp2(part[(r * S + j) * 2] - R);
+        sm.R[r] = R;
+        sm.Z[r] = Z;
+    }
+    __syncthreads();
+    finish_stochastic<DT, VEC, NT>(p, b, sq, sm);
+}
+
 // Row-split stochastic finish, in two kernels so that the closing-token draw
 // -- one or two full rows per sequence -- is spread over SD workgroups per
 // sequence instead of one:
@@ -1647,6 +1671,10 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
     if (e) return e;
     if (p.slice_draw) return launch1(k_sample_draw<DT, VEC>, p, p.B, NT_SAMPLE, stream);
+    if (p.B >= kSeqWideMinB)
+        return launch1(k_stochastic_finish<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
+    if (p.B >= kFinishOneGroupMinB)
+        return launch1(k_stochastic_finish<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
     e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
     if (e) return e;
     return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);

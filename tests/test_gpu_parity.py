@@ -411,6 +411,9 @@ RAGGED_CASES = [
     (200, 8, 1000, W.BF16, 1.0, 0, False, None),
     (256, 4, 20011, W.F32, 0.7, 0, True, "neginf"),
     (300, 2, 9, W.BF16, 1.0, 2, False, "oov"),
+    # with diagnostics these take row statistics, then one finishing
+    # workgroup per sequence (1024 threads at B = 256, 512 above)
+    (600, 6, 4103, W.BF16, 0.9, 0, False, None),
 ]
 
 
