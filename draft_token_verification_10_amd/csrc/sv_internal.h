@@ -13,16 +13,19 @@ constexpr int kMaxRowsPerSeq = 1024;
 
 // Two ways to lay the work out on the GPU:
 //
-//  * sequence-resident: one 1024-thread workgroup owns one sequence, streams
-//    all of its rows and finishes it in place.  Nothing crosses workgroups,
-//    so there are no atomics, fences or workspace.  Used when the batch alone
-//    fills the machine (single candidate, B >= kSeqResidentMinB).
+//  * sequence-resident: one workgroup (kSeqThreads or kSeqWideThreads
+//    threads, below) owns one sequence, streams all of its rows and finishes
+//    it in place.  Nothing crosses workgroups, so there are no atomics,
+//    fences or workspace.  Used when the batch alone fills the machine
+//    (single candidate, B >= kSeqResidentMinB).
 //
 //  * row-split: a statistics kernel gives every (row, slice) its own
-//    workgroup and writes 8 bytes per item to the workspace; a finishing
-//    kernel (one workgroup per sequence) merges them, decides and samples.
-//    The kernel boundary makes the statistics visible.  Used for small
-//    batches and for several candidates per sequence.
+//    workgroup and writes 8 bytes per item to the workspace; finishing
+//    kernels then merge them per sequence, decide and sample (the
+//    stochastic draw spread over several workgroups per sequence for small
+//    batches).  The kernel boundary makes the statistics visible.  Used for
+//    small batches, several candidates per sequence, draft trees, plain
+//    sampling outside the one-pass shapes and ragged batches read in full.
 constexpr int kSeqResidentMinB = 192;
 // Sequence-resident workgroup size: 1024 threads (one group per CU), or 512
 // threads once the sequences outnumber the 256 CUs, so that two or more share
@@ -31,8 +34,9 @@ constexpr int kSeqThreads = 1024;
 constexpr int kSeqWideThreads = 512;
 constexpr int kSeqWideMinB = 257;
 // Row-split stochastic calls with at least this many sequences (one per CU)
-// finish each sequence in one 1024-thread workgroup; smaller batches spread
-// the closing-token draw over SD workgroups per sequence instead.
+// finish each sequence in one workgroup (kSeqThreads threads, kSeqWideThreads
+// from kSeqWideMinB on); smaller batches spread the closing-token draw over SD
+// workgroups per sequence instead.
 constexpr int kFinishOneGroupMinB = 256;
 
 inline bool use_seq_resident(int B, int G) { return G == 1 && B >= kSeqResidentMinB; }
