@@ -24,7 +24,10 @@ Modes:
   commit      sv_commit of the workload's verified step (B sequences, k+1
               token slots): a launch-bound kernel, timed on its own
 
-Every HBM-bound line also carries "achievable_read": the rate of a plain
+Where rocprofv3 counts for the current kernel source are committed, each
+line and side object also gives "fetched_GBps": the rate on the bytes the
+counters saw moving (for early exit, the denominator that matches what it
+reads).  Every HBM-bound line also carries "achievable_read": the rate of a plain
 read with the same loads (sv_stream_read over 2 GiB) and the path's fraction
 of it, beside the fraction of the 8 TB/s peak.
 
@@ -309,16 +312,28 @@ def line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_config=Non
                      "traffic": traffic_for(traffic_key), "algorithmic_bytes": nbytes,
                      "kernel": kern},
         "wall_s_timed": round(wall, 3),
+        **fetched_rate(traffic_for(traffic_key), ms),
     }
+
+
+def fetched_rate(traffic, ms):
+    """GB/s and fraction of the peak on the bytes rocprofv3 counted moving
+    (null without counts for the current kernel source)."""
+    if traffic is None:
+        return {"fetched_GBps": None, "fetched_frac": None}
+    gbs = traffic / (ms * 1e-3) / 1e9
+    return {"fetched_GBps": round(gbs, 1), "fetched_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def side(spec, fns, nbytes, kern, traffic_key, args, torch, extra=None):
     ms, _ = time_calls(fns, args.steps, args.warmup, torch)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = traffic_for(traffic_key)
     out = {"value": round(spec.B / (ms * 1e-3), 1), "unit": "seqs/s",
            "ms_per_step": round(ms, 5), "algorithmic_bytes": nbytes,
            "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": kern,
-           "traffic": traffic_for(traffic_key)}
+           "traffic": traffic}
+    out.update(fetched_rate(traffic, ms))
     out.update(extra or {})
     return out
 

@@ -104,3 +104,9 @@ def test_cpu_baseline_reports_threads_and_single_thread():
     assert out["kind"] == "oracle" and out["cores"] == before and out["value"] > 0
     st = out["single_thread"]
     assert st["cores"] == 1 and st["value"] > 0 and st["unit"] == "seqs/s"
+
+
+def test_fetched_rate():
+    r = bench.fetched_rate(8e9, 1000.0)  # 8 GB in one second
+    assert r == {"fetched_GBps": 8.0, "fetched_frac": 0.001}
+    assert bench.fetched_rate(None, 1.0) == {"fetched_GBps": None, "fetched_frac": None}
