@@ -105,6 +105,18 @@ size_t rowsplit_need(int B, int rows_per_seq, int V, bool stochastic, bool sampl
     return sv::workspace_bytes_for(B, rows_per_seq, S, stochastic);
 }
 
+// Workspace of the capped early exit (still-accepting flags, then the
+// row-split stochastic layout with S slices per row).
+size_t exit_need(int B, int k, int S) {
+    return sv::exit_flag_bytes(B) + sv::workspace_bytes_for(B, 2 * k + 1, S, true);
+}
+
+int exit_slices_max(int V) {
+    int s = V / sv::kMinSliceElems;
+    if (s > sv::kExitMaxSlices) s = sv::kExitMaxSlices;
+    return s < 1 ? 1 : s;
+}
+
 }  // namespace
 
 // The library is built with hidden visibility; only the C ABI is exported.
@@ -117,8 +129,14 @@ size_t sv_workspace_bytes(int B, int G, int k, int V) {
     // candidate) may take the row-split layout (sampling outside the one-pass
     // shapes, ragged batches with diagnostics), and so do greedy calls below
     // the sequence-resident threshold and tree verification (G = N, k = 0).
-    const size_t s = rowsplit_need(B, 2 * k + 1, V, true, k == 0);
+    size_t s = rowsplit_need(B, 2 * k + 1, V, true, k == 0);
     const size_t g = rowsplit_need(B, G * (k + 1), V, false, false);
+    // and the capped early exit of dense and ragged stochastic calls, which
+    // only sequence-resident batches take
+    if (sv::plan_exit_pairs(k) > 0 && B >= sv::kSeqResidentMinB && B <= sv::kExitMaxB) {
+        const size_t e = exit_need(B, k, exit_slices_max(V));
+        if (e > s) s = e;
+    }
     return s > g ? s : g;
 }
 
@@ -138,6 +156,35 @@ const char* sv_status_string(int status) {
 }  // extern "C"
 
 namespace {
+
+// Sequence-resident early exit: when the caller's workspace has room, cap
+// the first pass at sv::plan_exit_pairs(k) pairs and finish in the row-split
+// layout (see sv_internal.h).  Without a workspace (allowed here) the plain
+// early exit runs, with the same decisions and tokens.
+void plan_exit(sv::Params* p, int E, void* workspace, size_t workspace_bytes) {
+    const int B = p->B, k = p->k, V = p->V;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || B > sv::kExitMaxB) return;
+    const int P = sv::plan_exit_pairs(k);
+    if (P < 1 || P >= k) return;
+    int smax = exit_slices_max(V);
+    while (smax > 1 && exit_need(B, k, smax) > workspace_bytes) --smax;
+    if (exit_need(B, k, smax) > workspace_bytes) return;
+    const int rows = 2 * k + 1;
+    char* w = static_cast<char*>(workspace);
+    p->active = reinterpret_cast<int*>(w);
+    w += sv::exit_flag_bytes(B);
+    p->part = reinterpret_cast<float*>(w);
+    w += sv::part_bytes(B, rows, smax);
+    p->tilesum = reinterpret_cast<float*>(w);
+    w += sv::tilesum_bytes(B);
+    p->meta = reinterpret_cast<int*>(w);
+    w += sv::meta_bytes(B);
+    p->xl = reinterpret_cast<float*>(w);
+    p->exit_pairs = P;
+    p->rows_per_seq = rows;
+    p->S = smax;
+    p->SD = sv::plan_draw_slices(B, sv::draw_tiles(V / E, V % E));
+}
 
 // Shared body of the stochastic entry points.  cu == nullptr: dense batch of
 // k draft tokens per sequence; else ragged (k is the maximum).  accept_len
@@ -202,6 +249,8 @@ int stochastic_impl(const void* target, const void* draft, const int32_t* x, con
     p.S = pl.S;
     p.slice_len = pl.slice_len;
     p.c = (float)c;
+    if (pl.seq && !dbg && k >= 2)
+        plan_exit(&p, pl.vec ? 16 / elem_size(dtype) : 1, workspace, workspace_bytes);
     return sv::launch_stochastic(p, dtype, pl.vec, pl.seq, stream) == 0 ? SV_OK : SV_ERR_HIP;
 }
 

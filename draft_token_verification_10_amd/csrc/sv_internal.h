@@ -131,6 +131,33 @@ inline int plan_draw_slices(int B, int tiles) {
 
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Capped early exit with a spread continuation.  A sequence-resident
+// early-exit workgroup streams at most plan_exit_pairs(k) pairs, stopping at
+// the first rejection, and leaves the statistics of what it streamed in the
+// row-split layout.  The sequences that accepted every streamed pair (the few
+// that would otherwise keep one CU streaming long after the rest are done)
+// have their remaining rows streamed by a persistent row-split kernel spread
+// over the whole GPU; then the row-split draw kernels decide and draw every
+// sequence, each closing-token draw spread over several workgroups.  Used when
+// the caller passes a workspace (the plain early exit needs none) and B <=
+// kExitMaxB.
+constexpr int kExitMaxB = 1024;
+constexpr int kExitStatsGrid = 2048;     // persistent statistics groups (8 per CU)
+constexpr long long kExitTargetItems = 2048;
+constexpr int kExitMaxSlices = 16;
+// Pairs of the capped pass; 0: no capping.  Measured on B=256, V=128256
+// bf16 batches (peaked target, draft noise sigma 1.5): k=8 at 3 pairs 116
+// against 151 us plain, k=6 at 2 pairs 113 against 124 us; at k=4 and k=3
+// the plain early exit is faster (96 against 102 us, 140 against 142 us).
+#ifndef SV_EXIT_PAIRS
+inline int plan_exit_pairs(int k) { return k >= 8 ? 3 : (k >= 6 ? 2 : 0); }
+#else
+inline int plan_exit_pairs(int) { return SV_EXIT_PAIRS; }
+#endif
+// Its workspace: an int flag per sequence (1: accepted every pair of the
+// capped pass), then the row-split stochastic layout below.
+inline size_t exit_flag_bytes(int B) { return round256((size_t)B * 4); }
+
 // Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S],
 // then (stochastic only) tile sums float [B][kMaxTiles + 1], the per
 // sequence draw parameters int4 [B] and the logit at each row's draft token
@@ -173,6 +200,8 @@ struct Params {
     int S;                // row-split: slices per row
     int slice_len;        // row-split: elements per slice
     float c;              // log2(e) / temperature
+    int* active;          // capped early exit: [B] still-accepting flags, else null
+    int exit_pairs;       // capped early exit: pairs streamed by the first pass
 };
 
 // Launchers (sv_kernels.hip).  dtype: 0 float32, 1 bfloat16; vec: every row

@@ -668,6 +668,7 @@ struct TargetW {
 struct Seq {
     int k;
     long long t0, d0;
+    int pos0;  // position of row 0 within the sequence (a continuation's first pair)
 };
 
 __device__ __forceinline__ Seq seq_of(const Params& p, int b) {
@@ -687,6 +688,18 @@ __device__ __forceinline__ Seq seq_of(const Params& p, int b) {
         s.d0 = (long long)b * p.G * p.k;
         s.t0 = (long long)b * p.G * (p.k + 1);
     }
+    s.pos0 = 0;
+    return s;
+}
+
+// The rest of sequence b from position pos0 on (pos0 < its k): the same
+// rows, tokens and uniforms, starting pos0 pairs later.
+__device__ __forceinline__ Seq seq_from(const Params& p, int b, int pos0) {
+    Seq s = seq_of(p, b);
+    s.pos0 = pos0;
+    s.k -= pos0;
+    s.t0 += pos0;
+    s.d0 += pos0;
     return s;
 }
 
@@ -759,8 +772,9 @@ __device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin
     }
     __syncthreads();
     const int a = sm.a;
-    int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
-    for (int i = tid; i <= p.k; i += NT) {
+    // a continuation (s.pos0 > 0) writes its own positions only
+    int32_t* out = p.tokens_out + (size_t)b * (p.k + 1) + s.pos0;
+    for (int i = tid; i <= p.k - s.pos0; i += NT) {
         if (i < a) out[i] = x[i];
         else if (i > a) out[i] = -1;
     }
@@ -787,7 +801,7 @@ __device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin
     }
     if (tid == 0) {
         out[a] = y;
-        if (p.accept_len) p.accept_len[b] = a;
+        if (p.accept_len) p.accept_len[b] = s.pos0 + a;
     }
 }
 
@@ -934,8 +948,14 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
         gu = p.u_accept[sq.d0 + lane];
     }
     int a = k;
+    // Capped (p.active set): stream at most p.exit_pairs pairs, leave every
+    // streamed row's statistics and the logits at the draft tokens in the
+    // row-split layout, and draw nothing; the continuation kernels finish.
+    const bool capped = p.active != nullptr;
+    const int npairs = capped ? min(p.exit_pairs, k) : k;
+    float* part = capped ? p.part + (size_t)b * p.rows_per_seq * p.S * 2 : nullptr;
     float Rt = 0.0f, Zt = 1.0f, Rd = 0.0f, Zd = 1.0f;
-    for (int i = 0; i < k; ++i) {
+    for (int i = 0; i < npairs; ++i) {
         float* wR = sm.wR + (i & 1) * 2 * NW;
         float* wZ = sm.wZ + (i & 1) * 2 * NW;
         for (int half = 0; half < 2; ++half) {
@@ -958,12 +978,24 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             sm.uv[lane] = gu;
             sm.tv[lane] = gt;
             sm.dv[lane] = gd;
+            if (capped) {
+                float* xl = p.xl + (size_t)b * p.rows_per_seq;
+                xl[lane] = gt;
+                xl[k + 1 + lane] = gd;
+            }
         }
         // One barrier per pair; the partials are double-buffered by pair
         // parity, so the next pair never overwrites what is being read.
         __syncthreads();
         merge_row<NW>(wR, wZ, 0, Rt, Zt);
         merge_row<NW>(wR, wZ, 1, Rd, Zd);
+        if (capped && tid < 2 * p.S) {
+            // slice 0 holds the row's statistics, the other slices merge as empty
+            const int half = tid / p.S, j = tid - half * p.S;
+            float* d = part + ((size_t)(half == 0 ? i : k + 1 + i) * p.S + j) * 2;
+            d[0] = j == 0 ? (half == 0 ? Rt : Rd) : -FLT_MAX;
+            d[1] = j == 0 ? (half == 0 ? Zt : Zd) : 0.0f;
+        }
         const int xi = sm.xv[i];
         float pi = 0.0f, qi = 0.0f;
         if (xi >= 0 && xi < V) {
@@ -974,6 +1006,10 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             a = i;
             break;
         }
+    }
+    if (capped) {  // 1: every streamed pair accepted, the rest of the rows still to read
+        if (tid == 0) p.active[b] = a < npairs ? 0 : 1;
+        return;
     }
     int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
     for (int i = tid; i <= p.k; i += NT) {
@@ -1157,6 +1193,31 @@ __global__ __launch_bounds__(NT) void k_stochastic_finish(Params p) {
     finish_stochastic<DT, VEC, NT>(p, b, sq, sm);
 }
 
+// Continuation of a capped early exit (p.active set by k_stochastic_seq_exit,
+// which left the statistics of every row it streamed in p.part, slice 0, and
+// the logits at the draft tokens in p.xl): the sequences that accepted every
+// streamed pair have the rest of their rows -- the pairs from
+// min(exit_pairs, k_b) on and the bonus row -- streamed by this persistent
+// row-split kernel, so that a long accepted run is read by many CUs at once
+// instead of one.  Then k_draw_tiles / k_draw_select decide and draw every
+// sequence from the statistics, spreading each closing-token draw over
+// several workgroups.  p.part is [B][2k+1][p.S] float2; rows are cut into S2
+// <= p.S slices, S2 chosen from the number of still-accepting sequences, and
+// slices S2 .. p.S-1 are written empty so the merge over p.S slices is exact.
+template <int DT, bool VEC>
+__device__ __forceinline__ void exit_slicing(const Params& p, int n_active, int rows2, int& S2,
+                                             int& slice_len) {
+    constexpr int E = Chunk<DT, VEC>::E;
+    const long long items = (long long)n_active * rows2;
+    long long s = items > 0 ? (kExitTargetItems + items - 1) / items : 1;
+    if (s > p.S) s = p.S;
+    if (s < 1) s = 1;
+    const int chunks = (p.V + E - 1) / E;
+    const int per = (chunks + (int)s - 1) / (int)s;
+    slice_len = per * E;
+    S2 = (p.V + slice_len - 1) / slice_len;  // no empty slices; S2 <= s
+}
+
 // Row-split stochastic finish, in two kernels so that the closing-token draw
 // -- one or two full rows per sequence -- is spread over SD workgroups per
 // sequence instead of one:
@@ -1168,14 +1229,12 @@ __global__ __launch_bounds__(NT) void k_stochastic_finish(Params p) {
 //   k_draw_select (B groups): the tile scan and the scan inside one tile.
 constexpr int NT_DRAW = kDrawRound;
 
+// Group sd of the SD groups that draw sequence b (all threads call).
 template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
+__device__ void draw_tiles_group(const Params& p, int b, int sd, int SD, StochFin<NT_DRAW>& sm) {
     constexpr int NT = NT_DRAW;
     constexpr int NW = NT / 64;
     constexpr int E = Chunk<DT, VEC>::E;
-    __shared__ StochFin<NT> sm;
-    const int b = blockIdx.x / p.SD;
-    const int sd = blockIdx.x - b * p.SD;
     const int tid = threadIdx.x;
     const Seq sq = seq_of(p, b);
     const int k = sq.k, V = p.V, S = p.S;
@@ -1250,7 +1309,7 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     const Row<DT, VEC> tr(stoch_row<DT>(p, sq, a), V);
     const Row<DT, VEC> dr(stoch_row<DT>(p, sq, a < k ? k + 1 + a : a), V);
     const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
-    const int tps = (g.nt_all + p.SD - 1) / p.SD;
+    const int tps = (g.nt_all + SD - 1) / SD;
     const int t0 = sd * tps, t1 = min(g.nt_all, t0 + tps);
     if (t0 >= t1) return;  // uniform: this group has no tiles
     for (int t = tid; t < (t1 - t0) * NW; t += NT) sm.tile_part[t] = 0.0f;
@@ -1275,6 +1334,101 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
         for (int w = 0; w < NW; ++w) s += sm.tile_part[t * NW + w];
         ts[t0 + t] = s;
     }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
+    __shared__ StochFin<NT_DRAW> sm;
+    const int b = blockIdx.x / p.SD;
+    const int sd = blockIdx.x - b * p.SD;
+    draw_tiles_group<DT, VEC>(p, b, sd, p.SD, sm);
+}
+
+struct ExitStatsSmem {
+    Scratch<NT_ROW> sc;
+    unsigned long long masks[kExitMaxB / 64];
+    int map[kExitMaxB];
+};
+
+// Group `group` of `ngroups` persistent statistics groups (all threads call).
+template <int DT, bool VEC>
+__device__ void exit_stats_groups(const Params& p, int group, int ngroups, ExitStatsSmem& es) {
+    constexpr int NW = NT_ROW / 64;
+    Scratch<NT_ROW>& sc = es.sc;
+    unsigned long long* masks = es.masks;
+    int* map = es.map;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Compact the still-accepting sequences, in index order (the same map in
+    // every workgroup): one ballot per 64 flags, then popcount prefixes.
+    const int ng = (p.B + 63) / 64;
+    for (int g = wave; g < ng; g += NW) {
+        const int bb = g * 64 + lane;
+        const unsigned long long m = __ballot(bb < p.B && p.active[bb] != 0);
+        if (lane == 0) masks[g] = m;
+    }
+    __syncthreads();
+    int n_active = 0;
+    for (int g = 0; g < ng; ++g) n_active += __popcll(masks[g]);
+    for (int g = wave; g < ng; g += NW) {
+        int pre = 0;
+        for (int h = 0; h < g; ++h) pre += __popcll(masks[h]);
+        const unsigned long long m = masks[g];
+        if ((m >> lane) & 1ull) map[pre + __popcll(m & ((1ull << lane) - 1ull))] = g * 64 + lane;
+    }
+    // rows left per sequence: at most 2 (k - min(exit_pairs, k)) + 1
+    const int rows2 = 2 * (p.k - min(p.exit_pairs, p.k)) + 1;
+    int S2, slice_len;
+    exit_slicing<DT, VEC>(p, n_active, rows2, S2, slice_len);
+    __syncthreads();
+    const int per_seq = rows2 * S2;
+    const long long items = (long long)n_active * per_seq;
+    for (long long it = group; it < items; it += ngroups) {
+        const int j = (int)(it / per_seq);
+        const int rem = (int)(it - (long long)j * per_seq);
+        const int r = rem / S2;
+        const int sl = rem - r * S2;
+        const int b = map[j];
+        const int kb = seq_of(p, b).k;
+        const Seq sq = seq_from(p, b, min(p.exit_pairs, kb));
+        if (r >= 2 * sq.k + 1) continue;  // row absent (ragged): uniform in the group
+        // the row's index in the sequence's full layout (draft rows after k_b + 1)
+        const int ra = r <= sq.k ? sq.pos0 + r : kb + 1 + sq.pos0 + (r - sq.k - 1);
+        const int v0 = sl * slice_len;
+        const int v1 = min(p.V, v0 + slice_len);
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, r) + (size_t)v0 * elem_bytes<DT>(), v1 - v0);
+        SoftAcc acc;
+        stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
+        float R, Z;
+        wave_softmax(acc, R, Z);
+        if (lane == 0) {
+            sc.f[wave] = R;
+            sc.g[wave] = Z;
+        }
+        __syncthreads();
+        float* dst = p.part + ((size_t)b * p.rows_per_seq + ra) * p.S * 2;
+        if (tid == 0) {
+            float RR = sc.f[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) RR = fmaxf(RR, sc.f[w]);
+            float ZZ = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) ZZ += sc.g[w] * fast_exp2(sc.f[w] - RR);
+            dst[sl * 2] = RR;
+            dst[sl * 2 + 1] = ZZ;
+        }
+        if (sl == 0)
+            for (int e = S2 + tid; e < p.S; e += NT_ROW) {
+                dst[e * 2] = -FLT_MAX;
+                dst[e * 2 + 1] = 0.0f;
+            }
+        __syncthreads();  // sc is reused by the next item
+    }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(NT_ROW) void k_exit_stats(Params p) {
+    __shared__ ExitStatsSmem es;
+    exit_stats_groups<DT, VEC>(p, blockIdx.x, gridDim.x, es);
 }
 
 // Plain sampling of row r from the statistics kernel's slice normalisers:
@@ -1660,6 +1814,17 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         return p.B >= kSeqWideMinB
                    ? launch1(k_sample_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
                    : launch1(k_sample_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
+    if (seq && p.active) {  // capped early exit, then the spread continuation
+        const bool wide = p.B >= kSeqWideMinB;
+        int e = wide ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
+        if (e) return e;
+        e = launch1(k_exit_stats<DT, VEC>, p, kExitStatsGrid, NT_ROW, stream);
+        if (e) return e;
+        e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
+        if (e) return e;
+        return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);
+    }
     if (seq && p.B >= kSeqWideMinB)
         return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
                      : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE,

@@ -64,7 +64,8 @@
  * plus a few bytes per row and per sequence.  Pass at least that many bytes,
  * 256-byte aligned.  Dense verification calls with k >= 1 need none when the
  * batch fills the GPU on its own (one candidate and B >= 192: every sequence
- * is then verified by a single workgroup), and accept NULL with size 0 there;
+ * is then verified by a single workgroup), and accept NULL with size 0 there
+ * (stochastic calls without diagnostics are faster with one, see below);
  * so does sv_sample with u when it samples each row in one pass (see
  * sv_sample).  Any
  * other call given NULL returns SV_ERR_NULL, and one given too few or
@@ -131,7 +132,13 @@ extern "C" {
  * own workgroup (B >= 192) stops reading a sequence at its first rejection
  * (the "early termination" of Novita's verification strategy, read as
  * stopping at the first mismatch); with dbg_px_qx every position of every
- * sequence is evaluated.  The outputs are the same either way.
+ * sequence is evaluated.  The outputs are the same either way.  Given a
+ * workspace of sv_workspace_bytes(B, 1, k, V) bytes, batches with 192 <= B
+ * <= 1024 and k >= 6 use it to keep the few sequences that accept a long run
+ * from holding the GPU: each sequence's own workgroup streams at most its
+ * first few pairs, and the rows of the sequences still accepting after them
+ * are then spread over all compute units (with NULL, 0 the single-workgroup
+ * early exit runs instead, with the same decisions and tokens).
  */
 int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept,
@@ -175,7 +182,8 @@ int sv_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
  * own k would be.  Malformed cu_draft_len values cannot make the library
  * read outside buffers of the stated sizes (they are clamped on the device),
  * but give undefined results.  draft_logits, draft_tokens and u_accept may
- * be NULL when total_draft == 0.  Workspace: sv_workspace_bytes(B, 1, k_max, V).
+ * be NULL when total_draft == 0.  Workspace: sv_workspace_bytes(B, 1, k_max, V)
+ * (the capped early exit of sv_verify_stochastic applies with k_max for k).
  */
 int sv_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const int32_t* cu_draft_len,

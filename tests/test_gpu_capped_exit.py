@@ -1,0 +1,151 @@
+"""GPU parity of the capped early exit.
+
+Stochastic calls without diagnostics, with 192..1024 sequences and k >= 6
+draft tokens, given a workspace: a first pass streams at most a few pairs per
+sequence (one workgroup each, stopping at the first rejection), the sequences
+that accepted all of them have their remaining rows streamed by a persistent
+row-split kernel, and the row-split draw kernels finish every sequence.  The
+same call without a workspace (NULL, 0) takes the plain early exit.  Both are
+checked against the float64 oracle by the stochastic agreement rules, and
+against each other: they must agree wherever the oracle's decisions and CDF
+breakpoints are further than 1e-5 from the uniforms.
+"""
+import numpy as np
+import pytest
+import torch
+
+from draft_token_verification_10_amd import binding
+from draft_token_verification_10_amd import workloads as W
+from oracle import protocol
+from test_gpu_parity import dev, logits_to_device, make_ragged, make_stochastic
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _empty():
+    """An empty tensor: the binding passes it as (NULL, 0)."""
+    return torch.empty(0, dtype=torch.uint8, device=DEV)
+
+
+def _compare(rep_a, rep_b, a1, t1, a2, t2):
+    """Capped and plain calls must agree except where either needed a band."""
+    if rep_a.decision_band or rep_a.token_band or rep_b.decision_band or rep_b.token_band:
+        return
+    assert np.array_equal(a1, a2)
+    assert np.array_equal(t1, t2)
+
+
+def run_dense(t, d, x, ua, us, tau, dtype, pad=0, unaligned=False, workspace="default"):
+    B, k1, V = t.shape
+    k = k1 - 1
+    tt, th, rs = logits_to_device(t, dtype, pad, unaligned)
+    dt, dh, _ = logits_to_device(d, dtype, pad, unaligned)
+    xd, uad, usd = dev(x), dev(ua), dev(us)
+    ws = None if workspace == "default" else workspace
+    a1, t1 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau, workspace=ws)
+    a2, t2 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau, workspace=_empty())
+    torch.cuda.synchronize()
+    kw = dict(B=B, k=k, V=V, temperature=tau, row_stride=rs)
+    r1 = protocol.compare_stochastic(th, dh, x, ua, us, accept_len=a1.cpu().numpy(),
+                                     tokens=t1.cpu().numpy(), **kw)
+    r2 = protocol.compare_stochastic(th, dh, x, ua, us, accept_len=a2.cpu().numpy(),
+                                     tokens=t2.cpu().numpy(), **kw)
+    return r1, r2, (a1.cpu().numpy(), t1.cpu().numpy(), a2.cpu().numpy(), t2.cpu().numpy())
+
+
+CASES = [
+    # (B, k, V, dtype, tau, pad, unaligned, special)
+    (256, 8, 4103, W.BF16, 1.0, 0, False, None),           # 3 pairs, 1024-thread groups
+    (256, 8, 4103, W.BF16, 1.0, 0, False, "close"),        # most sequences continue
+    (256, 8, 2053, W.F32, 1.0, 0, False, "equal"),         # every sequence continues to the bonus
+    (256, 8, 2053, W.BF16, 1.0, 0, False, "onehot"),       # nearly all reject at position 0
+    (192, 6, 1000, W.BF16, 0.7, 0, False, "close"),        # 2 pairs, the smallest batch
+    (300, 7, 4103, W.F32, 1.0, 3, False, "close"),         # 512-thread groups, padded rows
+    (512, 9, 3001, W.BF16, 1.3, 0, True, "close"),         # element-wise loads
+    (1024, 8, 513, W.BF16, 1.0, 0, False, "close"),        # the largest capped batch
+    (1025, 8, 513, W.BF16, 1.0, 0, False, "close"),        # one past it: the plain early exit
+    (200, 64, 300, W.F32, 1.0, 0, False, "close"),         # the longest draft
+    (256, 8, 2053, W.F32, 1.0, 0, False, "neginf"),
+    (256, 8, 2053, W.BF16, 1.0, 0, False, "oov"),
+    (192, 8, 32000, W.BF16, 1.0, 0, False, "close"),       # a long row, sliced by the continuation
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_k{}_V{}_{}_t{}_p{}_u{}_{}".format(
+    c[0], c[1], c[2], "bf16" if c[3] else "f32", c[4], c[5], int(c[6]), c[7]))
+def test_capped_dense(case):
+    B, k, V, dtype, tau, pad, unal, special = case
+    print(f"capped case {case}", flush=True)
+    seed = 4100 + CASES.index(case)
+    t, d, x, ua, us = make_stochastic(seed, B, k, V, dtype, tau, special=special)
+    r1, r2, (a1, t1, a2, t2) = run_dense(t, d, x, ua, us, tau, dtype, pad, unal)
+    print("capped", r1.summary(), "| plain", r2.summary(), "| accept_len histogram",
+          np.bincount(a1, minlength=k + 1).tolist())
+    assert r1.ok(), r1.summary()
+    assert r2.ok(), r2.summary()
+    _compare(r1, r2, a1, t1, a2, t2)
+
+
+def test_capped_small_workspace_falls_back():
+    """A workspace too small for the capped layout: the plain early exit runs
+    (same results), and a misaligned one is treated the same way."""
+    B, k, V, dtype, tau = 256, 8, 4103, W.BF16, 1.0
+    t, d, x, ua, us = make_stochastic(4200, B, k, V, dtype, tau, special="close")
+    small = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    r1, r2, (a1, t1, a2, t2) = run_dense(t, d, x, ua, us, tau, dtype, workspace=small)
+    assert r1.ok() and r2.ok(), (r1.summary(), r2.summary())
+    _compare(r1, r2, a1, t1, a2, t2)
+    big = torch.empty(binding.sv_workspace_bytes(B, 1, k, V) + 256, dtype=torch.uint8, device=DEV)
+    r1, r2, (a1, t1, a2, t2) = run_dense(t, d, x, ua, us, tau, dtype, workspace=big[16:])
+    assert r1.ok() and r2.ok(), (r1.summary(), r2.summary())
+    _compare(r1, r2, a1, t1, a2, t2)
+
+
+def test_capped_repeated_calls_reuse_workspace():
+    """The flags and statistics left in the workspace by one call never leak
+    into the next: a batch where every sequence continues, then one where
+    none does, then the first again, on the same workspace."""
+    B, k, V, dtype, tau = 256, 8, 2053, W.BF16, 1.0
+    ws = torch.empty(binding.sv_workspace_bytes(B, 1, k, V), dtype=torch.uint8, device=DEV)
+    for special in ("equal", "onehot", "equal", "close"):
+        t, d, x, ua, us = make_stochastic(4300, B, k, V, dtype, tau, special=special)
+        r1, r2, (a1, t1, a2, t2) = run_dense(t, d, x, ua, us, tau, dtype, workspace=ws)
+        assert r1.ok() and r2.ok(), (special, r1.summary(), r2.summary())
+        _compare(r1, r2, a1, t1, a2, t2)
+
+
+RAGGED = [
+    # (B, k_max, V, dtype, tau, lengths)
+    (256, 8, 4103, W.BF16, 1.0, "mixed"),     # k_b in 0..8: below, at and above 3 pairs
+    (300, 6, 2053, W.F32, 0.8, "mixed"),      # 2 pairs, 512-thread groups
+    (256, 8, 1000, W.BF16, 1.0, "short"),     # every k_b <= 3: the capped pass finishes all
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "B{}_k{}_V{}_{}_t{}_{}".format(
+    c[0], c[1], c[2], "bf16" if c[3] else "f32", c[4], c[5]))
+def test_capped_ragged(case):
+    B, k_max, V, dtype, tau, lengths = case
+    print(f"capped ragged case {case}", flush=True)
+    rng = np.random.default_rng(4400 + RAGGED.index(case))
+    kb = rng.integers(0, (k_max if lengths == "mixed" else 3) + 1, size=B)
+    cu, t, d, x, ua, us = make_ragged(4400 + RAGGED.index(case), B, k_max, V, dtype, tau, kb=kb)
+    n = int(cu[-1])
+    tt, th, rs = logits_to_device(t, dtype)
+    dt, dh, _ = logits_to_device(d, dtype)
+    cud, xd, uad, usd = dev(cu), dev(x), dev(ua), dev(us)
+    a1, t1 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau)
+    a2, t2 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau,
+                                                 workspace=_empty())
+    torch.cuda.synchronize()
+    kw = dict(k_max=k_max, V=V, temperature=tau, row_stride=rs)
+    r1 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a1.cpu().numpy(),
+                                            tokens=t1.cpu().numpy(), **kw)
+    r2 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a2.cpu().numpy(),
+                                            tokens=t2.cpu().numpy(), **kw)
+    print(n, "draft rows;", "capped", r1.summary(), "| plain", r2.summary())
+    assert r1.ok(), r1.summary()
+    assert r2.ok(), r2.summary()
+    _compare(r1, r2, a1.cpu().numpy(), t1.cpu().numpy(), a2.cpu().numpy(), t2.cpu().numpy())
