@@ -10,7 +10,7 @@ from draft_token_verification_10_amd import binding
 from draft_token_verification_10_amd import workloads as W
 from oracle import svo
 from tests.oracle_pins import random_tree
-from tests.test_gpu_parity import DEV, dev, logits_to_device
+from tests.test_gpu_parity import DEV, dev, logits_to_device, stable_seed
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,7 @@ TREE_CASES = [
 def test_tree(case):
     B, N, V, dtype, pad, unal, ties, deep = case
     print(f"tree case {case}", flush=True)
-    t, x, par = make_tree(hash(case) & 0xFFFF, B, N, V, dtype, ties, deep,
+    t, x, par = make_tree(stable_seed(case), B, N, V, dtype, ties, deep,
                           follow=0.97 if deep else 0.7)
     tt, th, rs = logits_to_device(t, dtype, pad, unal)
     a, tok, path = binding.sv_verify_greedy_tree(tt, dev(x), dev(par))
