@@ -38,6 +38,9 @@ figures); "warm" repeats the timing on one copy.
 Other switches, for the profiler:
   --copy-calibration   time a plain device-to-device copy of 1 GiB (the
                        reference kernel for HBM byte counters)
+  --record-traffic KEY --fetch-csv F --write-csv W --kernels K1,K2 [--source S]
+                       (no GPU) store one call's HBM bytes from a FETCH_SIZE
+                       and a WRITE_SIZE rocprofv3 run in profiles/traffic.json
   --no-cpu-baseline    skip the CPU oracle timing
 """
 from __future__ import annotations
@@ -146,6 +149,60 @@ def traffic_for(key: str):
     if not e or e.get("kernel_sha") != kernel_hash():
         return None
     return e.get("bytes_per_launch")
+
+
+def counter_kib(csv_path: str, kernel: str) -> float:
+    """Median over dispatches of the counter in a rocprofv3 counter-collection
+    CSV (one counter per run), for the kernels whose name contains `kernel`."""
+    import csv
+    import statistics
+    vals = []
+    with open(csv_path, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel!r} in {csv_path}")
+    return statistics.median(vals)
+
+
+def record_traffic(key: str, fetch_csv: str, write_csv: str, kernels: list, source: str) -> dict:
+    """Store the HBM bytes one call moves, from a FETCH_SIZE run and a
+    WRITE_SIZE run of rocprofv3 (KiB per dispatch, summed over the call's
+    kernels), in profiles/traffic.json under `key` with the kernel source
+    hash.  Key "_calibration" takes a plain 1 GiB device copy
+    (bench.py --copy-calibration) and stores the factor that turns each
+    counter into bytes; the other keys are scaled by it."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        tr = {}
+    fk = sum(counter_kib(fetch_csv, k) for k in kernels)
+    wk = sum(counter_kib(write_csv, k) for k in kernels)
+    if key == "_calibration":
+        n = 1 << 30
+        entry = {"kernel": " + ".join(kernels), "copy_bytes": n,
+                 "fetch_kib": fk, "write_kib": wk,
+                 "fetch_scale": round(n / (fk * 1024), 5), "write_scale": round(n / (wk * 1024), 5),
+                 "source": source}
+    else:
+        cal = tr.get("_calibration")
+        if not cal:
+            raise SystemExit("record the copy calibration (key _calibration) first")
+        fb = int(round(fk * 1024 * cal["fetch_scale"]))
+        wb = int(round(wk * 1024 * cal["write_scale"]))
+        entry = {"kernel": " + ".join(kernels), "kernel_sha": kernel_hash(),
+                 "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                 "bytes_per_launch": fb + wb, "fetch_scale": cal["fetch_scale"],
+                 "write_scale": cal["write_scale"], "source": source}
+        if len(kernels) > 1:
+            entry["per"] = "call (all kernels of the call)"
+    tr[key] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(tr, f, indent=1)
+        f.write("\n")
+    return entry
 
 
 def logits_to_device(a, dtype, torch, dev):
@@ -443,7 +500,22 @@ def main():
                     help="input copies rotated between calls (default: enough to exceed 600 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-traffic", metavar="KEY", default=None,
+                    help="store a call's HBM bytes from two rocprofv3 counter CSVs (no GPU)")
+    ap.add_argument("--fetch-csv", default=None)
+    ap.add_argument("--write-csv", default=None)
+    ap.add_argument("--kernels", default=None,
+                    help="comma-separated kernel names of one call, as in the CSVs")
+    ap.add_argument("--source", default="", help="the profile summary quoting the counts")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        if not (args.fetch_csv and args.write_csv and args.kernels):
+            ap.error("--record-traffic needs --fetch-csv, --write-csv and --kernels")
+        e = record_traffic(args.record_traffic, args.fetch_csv, args.write_csv,
+                           args.kernels.split(","), args.source)
+        print(json.dumps({args.record_traffic: e}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verification of a batch shards over GPUs "

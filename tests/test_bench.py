@@ -114,3 +114,35 @@ def test_fetched_rate():
     r = bench.fetched_rate(8e9, 1000.0)  # 8 GB in one second
     assert r == {"fetched_GBps": 8.0, "fetched_frac": 0.001}
     assert bench.fetched_rate(None, 1.0) == {"fetched_GBps": None, "fetched_frac": None}
+
+
+def test_record_traffic(tmp_path, monkeypatch):
+    """Counter CSVs -> bytes per call: the copy calibration's factor, then a
+    two-kernel call summed over its kernels (median over dispatches), tagged
+    with the kernel source hash so a later source change voids it."""
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+
+    def csv_file(name, rows):
+        p = tmp_path / name
+        p.write_text("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n" +
+                     "".join(f"{i},{k},C,{v}\n" for i, (k, v) in enumerate(rows)))
+        return str(p)
+
+    gib_kib = (1 << 30) / 1024
+    fc = csv_file("fc.csv", [("__amd_rocclr_copyBuffer", gib_kib / 2)] * 3)
+    wc = csv_file("wc.csv", [("__amd_rocclr_copyBuffer", gib_kib)] * 3)
+    cal = bench.record_traffic("_calibration", fc, wc, ["__amd_rocclr_copyBuffer"], "cal")
+    assert cal["fetch_scale"] == 2.0 and cal["write_scale"] == 1.0
+    rows_f = [("void sv::k_a<1>(sv::Params)", 100.0), ("void sv::k_a_exit<1>(sv::Params)", 7.0),
+              ("void sv::k_b<1>(sv::Params)", 10.0), ("void sv::k_a<1>(sv::Params)", 102.0),
+              ("void sv::k_a<1>(sv::Params)", 1000.0), ("void sv::k_b<1>(sv::Params)", 12.0)]
+    rows_w = [(k, v / 10) for k, v in rows_f]
+    e = bench.record_traffic("x/y", csv_file("f.csv", rows_f), csv_file("w.csv", rows_w),
+                             ["sv::k_a<", "sv::k_b<"], "src")
+    # medians: k_a 102 (k_a_exit not matched), k_b 11
+    assert e["fetch_bytes_per_launch"] == int((102 + 11) * 1024 * 2)
+    assert e["write_bytes_per_launch"] == int(round((10.2 + 1.1) * 1024))
+    assert e["bytes_per_launch"] == e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
+    assert bench.traffic_for("x/y") == e["bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "other")
+    assert bench.traffic_for("x/y") is None
