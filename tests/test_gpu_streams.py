@@ -19,7 +19,7 @@ def bf16(a64):
 
 
 def make_calls(rng):
-    """Four different calls (entry points and layouts), each returning a
+    """Five different calls (entry points and layouts), each returning a
     function that runs it on a given stream into fresh outputs."""
     calls = []
     # row-split stochastic (B < 192)
@@ -72,6 +72,19 @@ def make_calls(rng):
         y2 = binding.sv_sample(rows2, u5, 1.0, workspace=ws, stream=s)
         return [y1, y2]
     calls.append(c3)
+    # capped early exit (B >= 192, k >= 6, no diagnostics, a workspace per stream)
+    B6, k6, V6 = 256, 8, 4103
+    t64 = rng.standard_normal((B6, k6 + 1, V6)) * 3
+    t6 = bf16(t64)
+    d6 = bf16(t64[:, :k6] + rng.standard_normal((B6, k6, V6)) * 0.05)  # long accepted runs
+    x6 = torch.from_numpy(rng.integers(0, V6, (B6, k6)).astype(np.int32)).to(DEV)
+    ua6 = torch.from_numpy(W.exact_uniforms(rng, B6 * k6).reshape(B6, k6)).to(DEV)
+    us6 = torch.from_numpy(W.exact_uniforms(rng, B6)).to(DEV)
+
+    def c4(s):
+        ws = torch.empty(binding.sv_workspace_bytes(B6, 1, k6, V6), dtype=torch.uint8, device=DEV)
+        return list(binding.sv_verify_stochastic(t6, d6, x6, ua6, us6, 1.0, workspace=ws, stream=s))
+    calls.append(c4)
     return calls
 
 

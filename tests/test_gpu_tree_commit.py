@@ -173,11 +173,12 @@ def test_graph_replays_match_eager():
     """The library's launches captured in a HIP graph (as bench.py does for
     launch-bound calls): several replays, with eager work and synchronisation
     in between, each give exactly the eager outputs.  Covers the stochastic
-    row-split and sequence-resident layouts, sampling and commit."""
+    row-split and sequence-resident layouts (plain and capped early exit),
+    sampling and commit."""
     from tests.test_gpu_parity import make_stochastic
     cases = []
-    for B in (5, 200):
-        t, d, x, ua, us = make_stochastic(B + 11, B, 3, 4103, W.BF16, 1.0)
+    for B, k in ((5, 3), (200, 3), (200, 8)):
+        t, d, x, ua, us = make_stochastic(B + k + 8, B, k, 4103, W.BF16, 1.0, special="close")
         tt, _, _ = logits_to_device(t, W.BF16)
         dt, _, _ = logits_to_device(d, W.BF16)
         cases.append((tt, dt, dev(x), dev(ua), dev(us)))
@@ -198,7 +199,7 @@ def test_graph_replays_match_eager():
 
     for i, (tt, _, _, _, _) in enumerate(cases):
         outs[f"a{i}"] = torch.full((tt.shape[0],), -9, dtype=torch.int32, device=DEV)
-        outs[f"t{i}"] = torch.full((tt.shape[0], 4), -9, dtype=torch.int32, device=DEV)
+        outs[f"t{i}"] = torch.full((tt.shape[0], tt.shape[1]), -9, dtype=torch.int32, device=DEV)
     outs["y"] = torch.full((64,), -9, dtype=torch.int32, device=DEV)
     eager = [r.clone() for r in run()]
     torch.cuda.synchronize()
