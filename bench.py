@@ -432,6 +432,7 @@ def bench_tree(args, torch, dev, binding, workloads):
                      "traffic": traffic_for("tree"), "algorithmic_bytes": nbytes,
                      "kernel": "k_row_stats"},
         "wall_s_timed": round(wall, 3),
+        **fetched_rate(traffic_for("tree"), ms),
         "per_call_us": per_call_us(fns, min(args.steps, 100), torch),
         "mean_accepted_depth": round(float(acc.float().mean().item()), 4),
     }
