@@ -9,8 +9,9 @@ Sonar through speculation", sections "Špekulatívne dekódovanie" and
     sum_v min(p_i(v), q_i(v));
   * the token emitted at position j (accepted draft, corrective or bonus),
     given the step reaches j, is distributed as p_j.
-Both layouts are exercised: one workgroup per sequence (B >= 192, with and
-without diagnostics) and row-split (batches of 191).  A chi-square statistic
+Every layout is exercised: one workgroup per sequence (B >= 192, with and
+without diagnostics), row-split (batches of 191), and the capped early exit
+(k = 8, batches of 1024, without diagnostics; with them, the full read).  A chi-square statistic
 beyond its 1e-6 tail, or a rate more than 5 sigma from its value, fails.
 """
 import numpy as np
@@ -73,16 +74,16 @@ def check_law(a, tok, p, q, k, label):
 
 
 @pytest.mark.parametrize("dtype", [W.F32, W.BF16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("layout", ["sequence", "row_split"])
+@pytest.mark.parametrize("layout", ["sequence", "row_split", "capped"])
 def test_emitted_token_law(dtype, layout):
     print(f"law dtype={dtype} layout={layout}", flush=True)
-    rng = np.random.default_rng(4242 + 7 * dtype + (layout == "row_split"))
-    V, k, tau = 16, 3, 0.8
+    rng = np.random.default_rng(4242 + 7 * dtype + ["sequence", "row_split", "capped"].index(layout))
+    V, k, tau = 16, (8 if layout == "capped" else 3), 0.8
     t = W.round_logits(rng.standard_normal((k + 1, V)) * 1.5, dtype)
     d = W.round_logits(W.as_f64(t[:k], dtype) + rng.standard_normal((k, V)), dtype)
     p = softmax64(W.as_f64(t, dtype), tau)
     q = softmax64(W.as_f64(d, dtype), tau)
-    N = 200_000 if layout == "sequence" else 191 * 300
+    N = {"sequence": 200_000, "row_split": 191 * 300, "capped": 1024 * 200}[layout]
     x = np.stack([draw(rng, q[i], N) for i in range(k)], axis=1)
     ua = W.exact_uniforms(rng, N * k).reshape(N, k)
     us = W.exact_uniforms(rng, N)
@@ -91,7 +92,7 @@ def test_emitted_token_law(dtype, layout):
     xd = torch.from_numpy(x).to(DEV)
     uad = torch.from_numpy(ua).to(DEV)
     usd = torch.from_numpy(us).to(DEV)
-    step = N if layout == "sequence" else 191
+    step = {"sequence": N, "row_split": 191, "capped": 1024}[layout]
     for diag in (True, False):
         a = torch.empty(N, dtype=torch.int32, device=DEV)
         tok = torch.empty((N, k + 1), dtype=torch.int32, device=DEV)
