@@ -20,6 +20,7 @@ struct Launch {
     int dtype = -1;
     bool vec = false, seq = false;
 } last;
+int fail_with = 0;  // nonzero: the launchers report this HIP error
 }  // namespace
 
 namespace sv {
@@ -29,7 +30,7 @@ int launch_stochastic(const Params& p, int dtype, bool vec, bool seq, void*) {
     last.dtype = dtype;
     last.vec = vec;
     last.seq = seq;
-    return 0;
+    return fail_with;
 }
 int launch_greedy(const Params& p, int dtype, bool vec, bool seq, void* s) {
     return launch_stochastic(p, dtype, vec, seq, s);
@@ -40,7 +41,7 @@ int launch_tree(const Params& p, int dtype, bool vec, void* s) {
 int launch_commit(const int32_t*, const int32_t*, int, int, int32_t*, int32_t*, long long, int,
                   int32_t*, long long, void*) {
     ++last.calls;
-    return 0;
+    return fail_with;
 }
 }  // namespace sv
 
@@ -155,6 +156,17 @@ int main() {
                            (int32_t*)fake(5), (int32_t*)fake(6), nullptr, nullptr, 0,
                            nullptr) == SV_ERR_DTYPE && last.calls == 0);
     CHECK(strlen(sv_status_string(SV_ERR_HIP)) > 0);
+    // a launch the HIP runtime refuses is reported as SV_ERR_HIP
+    fail_with = 98;  // hipErrorInvalidDeviceFunction, say
+    CHECK(stoch(256, 8, V, fake(8), sv_workspace_bytes(256, 1, 8, V), false) == SV_ERR_HIP);
+    CHECK(stoch(4, 8, V, fake(8), sv_workspace_bytes(4, 1, 8, V), true) == SV_ERR_HIP);
+    last = Launch{};
+    CHECK(sv_verify_greedy(fake(0), (const int32_t*)fake(2), 256, 1, 8, V, V, SV_DTYPE_BF16,
+                           (int32_t*)fake(5), (int32_t*)fake(6), nullptr, nullptr, 0,
+                           nullptr) == SV_ERR_HIP);
+    CHECK(sv_commit((const int32_t*)fake(2), (const int32_t*)fake(3), 4, 9, (int32_t*)fake(4),
+                    (int32_t*)fake(5), 64, 64, (int32_t*)fake(6), 1, nullptr) == SV_ERR_HIP);
+    fail_with = 0;
     if (fails) {
         fprintf(stderr, "%d checks failed\n", fails);
         return 1;
