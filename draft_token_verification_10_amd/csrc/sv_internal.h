@@ -146,11 +146,12 @@ constexpr int kExitStatsGrid = 2048;     // persistent statistics groups (8 per 
 constexpr long long kExitTargetItems = 2048;
 constexpr int kExitMaxSlices = 16;
 // Pairs of the capped pass; 0: no capping.  Measured on B=256, V=128256
-// bf16 batches (peaked target, draft noise sigma 1.5): k=8 at 3 pairs 116
-// against 151 us plain, k=6 at 2 pairs 113 against 124 us; at k=4 and k=3
-// the plain early exit is faster (96 against 102 us, 140 against 142 us).
+// bf16 batches (peaked target, draft noise sigma 1.5), 3 pairs against the
+// plain early exit: k=8 118 against 150 us, k=7 113 against 136 us, k=6 110
+// against 122 us (2 pairs: 122, 116, 109 us); at k=4 and k=3 the plain early
+// exit is faster (95 against 102 us, 140 against 142 us).
 #ifndef SV_EXIT_PAIRS
-inline int plan_exit_pairs(int k) { return k >= 8 ? 3 : (k >= 6 ? 2 : 0); }
+inline int plan_exit_pairs(int k) { return k >= 6 ? 3 : 0; }
 #else
 inline int plan_exit_pairs(int) { return SV_EXIT_PAIRS; }
 #endif

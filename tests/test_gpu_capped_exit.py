@@ -61,7 +61,7 @@ CASES = [
     (256, 8, 4103, W.BF16, 1.0, 0, False, "close"),        # most sequences continue
     (256, 8, 2053, W.F32, 1.0, 0, False, "equal"),         # every sequence continues to the bonus
     (256, 8, 2053, W.BF16, 1.0, 0, False, "onehot"),       # nearly all reject at position 0
-    (192, 6, 1000, W.BF16, 0.7, 0, False, "close"),        # 2 pairs, the smallest batch
+    (192, 6, 1000, W.BF16, 0.7, 0, False, "close"),        # k = 6, the smallest batch
     (300, 7, 4103, W.F32, 1.0, 3, False, "close"),         # 512-thread groups, padded rows
     (512, 9, 3001, W.BF16, 1.3, 0, True, "close"),         # element-wise loads
     (1024, 8, 513, W.BF16, 1.0, 0, False, "close"),        # the largest capped batch
@@ -119,7 +119,7 @@ def test_capped_repeated_calls_reuse_workspace():
 RAGGED = [
     # (B, k_max, V, dtype, tau, lengths)
     (256, 8, 4103, W.BF16, 1.0, "mixed"),     # k_b in 0..8: below, at and above 3 pairs
-    (300, 6, 2053, W.F32, 0.8, "mixed"),      # 2 pairs, 512-thread groups
+    (300, 6, 2053, W.F32, 0.8, "mixed"),      # k_max = 6, 512-thread groups
     (256, 8, 1000, W.BF16, 1.0, "short"),     # every k_b <= 3: the capped pass finishes all
 ]
 
