@@ -133,17 +133,25 @@ inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 // Capped early exit with a spread continuation.  A sequence-resident
 // early-exit workgroup streams at most plan_exit_pairs(k) pairs, stopping at
-// the first rejection, and leaves the statistics of what it streamed in the
-// row-split layout.  The sequences that accepted every streamed pair (the few
+// the first rejection, draws the token of a sequence rejected at position 0
+// itself, and leaves the statistics of what it streamed in the row-split
+// layout.  The sequences that accepted every streamed pair (the few
 // that would otherwise keep one CU streaming long after the rest are done)
 // have their remaining rows streamed by a persistent row-split kernel spread
 // over the whole GPU; then the row-split draw kernels decide and draw every
-// sequence, each closing-token draw spread over several workgroups.  Used when
+// other sequence, each closing-token draw spread over several workgroups.  Used when
 // the caller passes a workspace (the plain early exit needs none) and B <=
 // kExitMaxB.
 constexpr int kExitMaxB = 1024;
 constexpr int kExitStatsGrid = 2048;     // persistent statistics groups (8 per CU)
 constexpr long long kExitTargetItems = 2048;
+// A sequence that the capped pass sees rejected at a position below this
+// draws its token in that pass (its CU is free long before the pass ends).
+#ifndef SV_EXIT_DRAW_HERE
+constexpr int kExitDrawHere = 1;
+#else
+constexpr int kExitDrawHere = SV_EXIT_DRAW_HERE;
+#endif
 constexpr int kExitMaxSlices = 16;
 // Pairs of the capped pass; 0: no capping.  Measured on B=256, V=128256
 // bf16 batches (peaked target, draft noise sigma 1.5), 3 pairs against the
@@ -155,8 +163,9 @@ inline int plan_exit_pairs(int k) { return k >= 6 ? 3 : 0; }
 #else
 inline int plan_exit_pairs(int) { return SV_EXIT_PAIRS; }
 #endif
-// Its workspace: an int flag per sequence (1: accepted every pair of the
-// capped pass), then the row-split stochastic layout below.
+// Its workspace: an int flag per sequence (0: rejected, drawn by the spread
+// draw; 1: accepted every pair of the capped pass; 2: finished by the capped
+// pass), then the row-split stochastic layout below.
 inline size_t exit_flag_bytes(int B) { return round256((size_t)B * 4); }
 
 // Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S],

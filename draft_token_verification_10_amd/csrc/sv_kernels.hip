@@ -950,7 +950,8 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     int a = k;
     // Capped (p.active set): stream at most p.exit_pairs pairs, leave every
     // streamed row's statistics and the logits at the draft tokens in the
-    // row-split layout, and draw nothing; the continuation kernels finish.
+    // row-split layout, and draw only after a rejection at an early position;
+    // the continuation kernels finish the rest.
     const bool capped = p.active != nullptr;
     const int npairs = capped ? min(p.exit_pairs, k) : k;
     float* part = capped ? p.part + (size_t)b * p.rows_per_seq * p.S * 2 : nullptr;
@@ -1007,9 +1008,14 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             break;
         }
     }
-    if (capped) {  // 1: every streamed pair accepted, the rest of the rows still to read
-        if (tid == 0) p.active[b] = a < npairs ? 0 : 1;
-        return;
+    if (capped) {
+        // 0: rejected, drawn by the spread draw kernels; 1: every streamed
+        // pair accepted, the rest of the rows still to read; 2: rejected
+        // early enough to draw here, off the critical path (the sequences
+        // that stream all the capped pairs take longer)
+        const bool here = a < npairs && a < kExitDrawHere;
+        if (tid == 0) p.active[b] = here ? 2 : (a < npairs ? 0 : 1);
+        if (!here) return;
     }
     int32_t* out = p.tokens_out + (size_t)b * (p.k + 1);
     for (int i = tid; i <= p.k; i += NT) {
@@ -1341,6 +1347,7 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_tiles(Params p) {
     __shared__ StochFin<NT_DRAW> sm;
     const int b = blockIdx.x / p.SD;
     const int sd = blockIdx.x - b * p.SD;
+    if (p.active && p.active[b] == 2) return;  // drawn by the capped pass
     draw_tiles_group<DT, VEC>(p, b, sd, p.SD, sm);
 }
 
@@ -1363,7 +1370,7 @@ __device__ void exit_stats_groups(const Params& p, int group, int ngroups, ExitS
     const int ng = (p.B + 63) / 64;
     for (int g = wave; g < ng; g += NW) {
         const int bb = g * 64 + lane;
-        const unsigned long long m = __ballot(bb < p.B && p.active[bb] != 0);
+        const unsigned long long m = __ballot(bb < p.B && p.active[bb] == 1);
         if (lane == 0) masks[g] = m;
     }
     __syncthreads();
@@ -1488,6 +1495,7 @@ __global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
     constexpr int E = Chunk<DT, VEC>::E;
     __shared__ StochFin<NT> sm;
     const int b = blockIdx.x;
+    if (p.active && p.active[b] == 2) return;  // drawn by the capped pass
     const Seq sq = seq_of(p, b);
     const int k = sq.k, V = p.V;
     const float c = p.c;

@@ -4,7 +4,8 @@ Stochastic calls without diagnostics, with 192..1024 sequences and k >= 6
 draft tokens, given a workspace: a first pass streams at most a few pairs per
 sequence (one workgroup each, stopping at the first rejection), the sequences
 that accepted all of them have their remaining rows streamed by a persistent
-row-split kernel, and the row-split draw kernels finish every sequence.  The
+row-split kernel, and the row-split draw kernels finish every sequence the
+first pass did not (it draws a rejection at position 0 itself).  The
 same call without a workspace (NULL, 0) takes the plain early exit.  Both are
 checked against the float64 oracle by the stochastic agreement rules, and
 against each other: they must agree wherever the oracle's decisions and CDF
