@@ -138,6 +138,51 @@ int main() {
         CHECK(last.seq && last.p.active != nullptr && last.p.cu != nullptr);
         check_capped_layout(fake(8), wsb, B, kmax);
     }
+    // the other layouts of the plan
+    {
+        const size_t big = (size_t)1 << 30;  // a workspace larger than any bound here
+        int32_t* o = (int32_t*)fake(5);
+        // greedy: one workgroup per sequence from 192 single candidates on
+        last = Launch{};
+        CHECK(sv_verify_greedy(fake(0), (const int32_t*)fake(2), 192, 1, 8, V, V, SV_DTYPE_BF16,
+                               o, o, nullptr, fake(8), big, nullptr) == SV_OK);
+        CHECK(last.seq);
+        CHECK(sv_verify_greedy(fake(0), (const int32_t*)fake(2), 191, 1, 8, V, V, SV_DTYPE_BF16,
+                               o, o, nullptr, fake(8), big, nullptr) == SV_OK);
+        CHECK(!last.seq);
+        // several candidates: always row-split (rows of all candidates spread)
+        CHECK(sv_verify_greedy(fake(0), (const int32_t*)fake(2), 512, 16, 4, 32000, 32000,
+                               SV_DTYPE_F32, o, o, nullptr, fake(8), big, nullptr) == SV_OK);
+        CHECK(!last.seq && last.p.G == 16 && last.p.rows_per_seq == 16 * 5);
+        // trees: row-split, one row per node
+        CHECK(sv_verify_greedy_tree(fake(0), (const int32_t*)fake(2), (const int32_t*)fake(3), 300,
+                                    64, V, V, SV_DTYPE_BF16, o, o, o, fake(8), big,
+                                    nullptr) == SV_OK);
+        CHECK(!last.seq && last.p.rows_per_seq == 64);
+        // ragged with diagnostics and unequal lengths: every row read, rows
+        // balanced over the GPU (row-split); with equal lengths, one group
+        // per sequence
+        CHECK(stoch(256, 8, V, fake(8), big, true, (const int32_t*)fake(9), 1000) == SV_OK);
+        CHECK(!last.seq && last.p.active == nullptr);
+        CHECK(stoch(256, 8, V, fake(8), big, true, (const int32_t*)fake(9), 256 * 8) == SV_OK);
+        CHECK(last.seq && last.p.active == nullptr);
+        // plain sampling: one pass per row where that layout is faster,
+        // else rows cut into slices drawn from their slice statistics
+        last = Launch{};
+        CHECK(sv_sample(fake(0), (const float*)fake(4), 256, V, V, SV_DTYPE_BF16, 1.0f, 0, o,
+                        fake(8), big, nullptr) == SV_OK);
+        CHECK(last.seq && last.p.k == 0);  // V <= 40960 + 352 * 256
+        CHECK(sv_sample(fake(0), (const float*)fake(4), 64, V, V, SV_DTYPE_BF16, 1.0f, 0, o,
+                        fake(8), big, nullptr) == SV_OK);
+        CHECK(!last.seq && last.p.slice_draw == 1 && last.p.S >= 8);
+        CHECK(sv_sample(fake(0), (const float*)fake(4), 512, 32000, 32000, SV_DTYPE_BF16, 1.0f, 0,
+                        o, nullptr, 0, nullptr) == SV_OK);  // one pass needs no workspace
+        CHECK(last.seq);
+        // argmax sampling is greedy verification of rows with no drafts
+        CHECK(sv_sample(fake(0), nullptr, 256, V, V, SV_DTYPE_BF16, 1.0f, 1, o, fake(8), big,
+                        nullptr) == SV_OK);
+        CHECK(last.seq && last.p.k == 0 && last.p.rows_per_seq == 1);
+    }
     // argument checks answer before any launch
     CHECK(stoch(-1, 8, V, nullptr, 0, false) == SV_ERR_SHAPE && last.calls == 0);
     CHECK(stoch(4, SV_MAX_K + 1, V, nullptr, 0, false) == SV_ERR_SHAPE && last.calls == 0);
