@@ -150,3 +150,55 @@ def test_capped_ragged(case):
     assert r1.ok(), r1.summary()
     assert r2.ok(), r2.summary()
     _compare(r1, r2, a1.cpu().numpy(), t1.cpu().numpy(), a2.cpu().numpy(), t2.cpu().numpy())
+
+
+def random_capped_cases(n=24, seed=778):
+    """Seeded shapes on the capped path: 192..1024 sequences, k in 6..16,
+    V from 2000 to 130000 (rows long enough to be sliced by the
+    continuation), dense and ragged, padded and unaligned rows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(192, 1025))
+        k = int(rng.choice([6, 7, 8, 9, 12, 16]))
+        V = int(np.exp(rng.uniform(np.log(2000), np.log(130000))))
+        while B * (2 * k + 1) * V > 60_000_000:
+            V //= 2
+        cases.append((i, B, k, V, int(rng.choice([W.F32, W.BF16])),
+                      float(rng.choice([0.5, 1.0, 1.7])),
+                      int(rng.integers(1, 4)) if rng.random() < 0.3 else 0,
+                      bool(rng.random() < 0.3),
+                      [None, "close", "equal", "onehot", "neginf", "oov"][int(rng.integers(0, 6))],
+                      bool(rng.random() < 0.4)))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_capped_cases(), ids=lambda c: "{}_B{}_k{}_V{}_{}_{}".format(
+    c[0], c[1], c[2], c[3], "bf16" if c[4] else "f32", "ragged" if c[9] else c[8]))
+def test_capped_random(case):
+    i, B, k, V, dtype, tau, pad, unal, special, ragged = case
+    print(f"capped random case {case}", flush=True)
+    seed = 4500 + i
+    if not ragged:
+        t, d, x, ua, us = make_stochastic(seed, B, k, V, dtype, tau, special=special)
+        r1, r2, (a1, t1, a2, t2) = run_dense(t, d, x, ua, us, tau, dtype, pad, unal)
+    else:
+        cu, t, d, x, ua, us = make_ragged(seed, B, k, V, dtype, tau)
+        tt, th, rs = logits_to_device(t, dtype, pad, unal)
+        dt, dh, _ = logits_to_device(d if int(cu[-1]) else np.zeros((1, V), t.dtype), dtype, pad,
+                                     unal)
+        cud, xd, uad, usd = dev(cu), dev(x), dev(ua), dev(us)
+        o1 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k, tau)
+        o2 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k, tau,
+                                                 workspace=_empty())
+        torch.cuda.synchronize()
+        a1, t1, a2, t2 = (o.cpu().numpy() for o in (*o1, *o2))
+        kw = dict(k_max=k, V=V, temperature=tau, row_stride=rs)
+        r1 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a1, tokens=t1,
+                                                **kw)
+        r2 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a2, tokens=t2,
+                                                **kw)
+    print("capped", r1.summary(), "| plain", r2.summary())
+    assert r1.ok(), r1.summary()
+    assert r2.ok(), r2.summary()
+    _compare(r1, r2, a1, t1, a2, t2)
