@@ -20,6 +20,8 @@ SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
 SV_MAX_K = 64
 SV_MAX_ROWS_PER_SEQ = 1024
+SV_ERR_SCRATCH = -7
+SV_SCRATCH_BYTES = 8 << 20
 
 _lib = None
 
@@ -57,6 +59,9 @@ def load(path: str | None = None):
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.sv_stream_read.argtypes = [P, SZ, I, P, P]
     lib.sv_stream_read.restype = I
+    lib.sv_verify_stochastic_noalloc.argtypes = [P, P, P, P, P, I, I, I, I64, I, ctypes.c_float,
+                                                 P, P, P, P]
+    lib.sv_verify_stochastic_noalloc.restype = I
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -178,6 +183,40 @@ def sv_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor
         _ptr(u_sample), B, k, V, rs, _dtype_code(target_logits), float(temperature),
         _ptr(accept_len), _ptr(tokens), _ptr(dbg_px_qx), _ptr(workspace), _ws_bytes(workspace),
         ctypes.c_void_p(s))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accept_len, tokens
+
+
+def sv_verify_stochastic_noalloc(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                 draft_tokens: torch.Tensor, u_accept: torch.Tensor,
+                                 u_sample: torch.Tensor, temperature: float = 1.0, *,
+                                 accept_len: torch.Tensor, tokens: torch.Tensor,
+                                 dbg_px_qx: torch.Tensor | None = None, stream=None):
+    """sv_verify_stochastic with the library's own per-GPU scratch buffer in
+    place of a workspace: the call allocates nothing, so the outputs must be
+    passed in.  Same shapes and results as sv_verify_stochastic."""
+    _dev(target_logits)
+    _dev(draft_logits)
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    if tuple(draft_logits.shape) != (B, k, V) or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("draft_logits must be [B][k][V] with the target's dtype")
+    rs = _row_stride(target_logits)
+    if B > 0 and _row_stride(draft_logits) != rs:
+        raise ValueError("target and draft rows must share one row stride")
+    _check_i32(draft_tokens, (B, k), "draft_tokens")
+    _check_f32(u_accept, (B, k), "u_accept")
+    _check_f32(u_sample, (B,), "u_sample")
+    _check_i32(accept_len, (B,), "accept_len")
+    _check_i32(tokens, (B, k + 1), "tokens")
+    if dbg_px_qx is not None:
+        _check_f32(dbg_px_qx, (B, k, 2), "dbg_px_qx")
+    s = stream if stream is not None else torch.cuda.current_stream(target_logits.device).cuda_stream
+    st = load().sv_verify_stochastic_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+        _ptr(u_sample), B, k, V, rs, _dtype_code(target_logits), float(temperature),
+        _ptr(accept_len), _ptr(tokens), _ptr(dbg_px_qx), ctypes.c_void_p(s))
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accept_len, tokens

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["sv_api.cpp", "sv_kernels.hip", "sv_measure.hip"]
+SOURCES = ["sv_api.cpp", "sv_kernels.hip", "sv_measure.hip", "sv_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -149,6 +149,7 @@ const char* sv_status_string(int status) {
         case SV_ERR_TEMPERATURE: return "temperature must be positive and finite";
         case SV_ERR_WORKSPACE: return "workspace smaller than sv_workspace_bytes() or not 256-byte aligned";
         case SV_ERR_HIP: return "the HIP runtime refused the kernel launch";
+        case SV_ERR_SCRATCH: return "the shape needs more workspace than the library's own buffer (SV_SCRATCH_BYTES) holds";
         default: return "unknown status";
     }
 }

@@ -102,6 +102,8 @@ extern "C" {
 #define SV_ERR_WORKSPACE (-5)   /* workspace smaller than required or not   */
                                 /* 256-byte aligned                         */
 #define SV_ERR_HIP (-6)         /* the HIP runtime refused the launch       */
+#define SV_ERR_SCRATCH (-7)     /* sv_verify_stochastic_noalloc: the shape  */
+                                /* needs more than SV_SCRATCH_BYTES         */
 
 /* Logit element types. */
 #define SV_DTYPE_F32 0
@@ -110,6 +112,9 @@ extern "C" {
 /* Limits. */
 #define SV_MAX_K 64               /* draft tokens per sequence (candidate)   */
 #define SV_MAX_ROWS_PER_SEQ 1024  /* G*(k+1) in greedy mode                 */
+/* Device memory the library holds on each GPU it runs on, for
+ * sv_verify_stochastic_noalloc: 8 MiB. */
+#define SV_SCRATCH_BYTES 8388608u
 
 /*
  * Stochastic verification of B sequences.
@@ -268,6 +273,27 @@ int sv_verify_greedy_tree(const void* target_logits, const int32_t* node_tokens,
 int sv_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W, int32_t* seq_len,
               int32_t* history, int64_t history_stride, int capacity, int32_t* next_token,
               int64_t next_stride, void* stream);
+
+/*
+ * sv_verify_stochastic without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * hosts that forbid hipMalloc.  Arguments, outputs and results are exactly
+ * those of sv_verify_stochastic given a workspace of sv_workspace_bytes(B, 1,
+ * k, V) bytes (same kernels, bit-identical outputs).  The workspace is a
+ * buffer of SV_SCRATCH_BYTES that the library holds on each GPU from the
+ * first call there until the process ends; this call allocates nothing.
+ * Shapes whose sv_workspace_bytes(B, 1, k, V) exceeds SV_SCRATCH_BYTES return
+ * SV_ERR_SCRATCH before anything is launched.  Every call on one GPU shares
+ * that GPU's buffer: calls that overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race.  The stream decides the
+ * GPU; NULL means the current device.
+ */
+int sv_verify_stochastic_noalloc(const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_tokens, const float* u_accept,
+                                 const float* u_sample, int B, int k, int V,
+                                 int64_t row_stride, int dtype, float temperature,
+                                 int32_t* accept_len, int32_t* tokens, float* dbg_px_qx,
+                                 void* stream);
 
 /* Workspace bytes that suffice for any entry point at this shape (G = 1 for
  * stochastic, ragged (k = k_max) and sampling (k = 0) calls; G = N, k = 0 for

@@ -13,6 +13,7 @@ HEADER = os.path.join(INCLUDE, "specverify.h")
 
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_TEMPERATURE, SV_ERR_WORKSPACE, SV_ERR_HIP = \
     0, -1, -2, -3, -4, -5, -6
+SV_ERR_SCRATCH = -7
 
 
 HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
@@ -49,7 +50,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["sv_commit", "sv_sample", "sv_status_string", "sv_stream_read",
                      "sv_verify_greedy", "sv_verify_greedy_ragged", "sv_verify_greedy_tree",
-                     "sv_verify_stochastic", "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
+                     "sv_verify_stochastic", "sv_verify_stochastic_noalloc",
+                     "sv_verify_stochastic_ragged", "sv_workspace_bytes"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -64,16 +66,18 @@ def test_header_constants_match_binding():
     assert c["SV_DTYPE_BF16"] == binding.SV_DTYPE_BF16
     assert c["SV_MAX_K"] == binding.SV_MAX_K
     assert c["SV_MAX_ROWS_PER_SEQ"] == binding.SV_MAX_ROWS_PER_SEQ
+    assert c["SV_ERR_SCRATCH"] == SV_ERR_SCRATCH == binding.SV_ERR_SCRATCH
+    assert c["SV_SCRATCH_BYTES"] == binding.SV_SCRATCH_BYTES == 8 << 20
 
 
 def test_status_strings(lib):
     seen = set()
     for st in (SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_TEMPERATURE,
-               SV_ERR_WORKSPACE, SV_ERR_HIP):
+               SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_SCRATCH):
         s = lib.sv_status_string(st).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert lib.sv_status_string(12345).decode() == "unknown status"
 
 
@@ -356,3 +360,24 @@ def test_stream_read_checks(lib):
     for blocks in (0, -1, 65537):
         assert lib.sv_stream_read(A, 16, blocks, out, None) == SV_ERR_SHAPE
     assert lib.sv_stream_read(A, 1 << 32, 1, out, None) == SV_ERR_SHAPE  # share above 2 GiB
+
+
+def test_noalloc_host_checks(lib):
+    """sv_verify_stochastic_noalloc refuses, before touching any device, a
+    shape whose workspace exceeds the library's own buffer, and passes every
+    other bad argument to the checks of sv_verify_stochastic."""
+    P = ctypes.c_void_p
+    f = lib.sv_verify_stochastic_noalloc
+    f.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_int, ctypes.c_float, P, P, P, P]
+    f.restype = ctypes.c_int
+    fake = P(1 << 40)
+    big = (1024, 64, 128256)
+    assert lib.sv_workspace_bytes(big[0], 1, big[1], big[2]) > binding.SV_SCRATCH_BYTES
+    assert f(fake, fake, fake, fake, fake, *big, big[2], 1, 1.0, fake, fake, None, None) == \
+        SV_ERR_SCRATCH
+    assert f(fake, fake, fake, fake, fake, 4, 65, 100, 100, 1, 1.0, fake, fake, None, None) == \
+        SV_ERR_SHAPE
+    assert f(fake, fake, fake, fake, fake, -1, 2, 100, 100, 1, 1.0, fake, fake, None, None) == \
+        SV_ERR_SHAPE
+    assert f(fake, fake, fake, fake, fake, 0, 2, 100, 100, 1, 1.0, fake, fake, None, None) == SV_OK
