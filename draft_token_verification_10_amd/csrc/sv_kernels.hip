@@ -541,7 +541,11 @@ __device__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const 
             const int t = tid * tpt + j;
             if (t < g.nt_all) {
                 tile_excl[t] = acc;
-                if (cross == INT_MAX && acc + mine[j] > T) cross = t;
+                // Only a tile with weight can hold the draw.  (A later, empty
+                // tile's prefix comes from the scan's own association and may
+                // exceed the last weighted tile's excl + sum by an ulp; taken
+                // as the crossing, its scan would find no token at all.)
+                if (cross == INT_MAX && mine[j] > 0.0f && acc + mine[j] > T) cross = t;
                 acc += mine[j];
             }
         }
@@ -549,24 +553,19 @@ __device__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const 
     cross = block_min_i<NT>(cross, sc);  // its barrier also publishes tile_excl
     *total_out = total;
     if (cross == INT_MAX) {
-        // Rounding left r * total at or above the last cumulative sum: take
-        // the last index with positive weight (a pass of its own: rare).
-        int lastpos = -1;
-        for (int ci = tid; ci < nch; ci += NT) {
-            const C tc = tr.chunk(ci);
-            C dc;
-            if (PAIR) dc = dr.chunk(ci);
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                if ((PAIR ? wf(tc.get(e), dc.get(e)) : wf(tc.get(e), 0.0f)) > 0.0f)
-                    lastpos = ci * E + e;
+        // No cumulative sum exceeds r * total (r = 1, or rounding left r *
+        // total at or above the last sum): the draw is the last index with
+        // positive weight.  It lies in the last tile with a positive sum
+        // (every weight after it is zero), so pass B scans that tile like a
+        // crossing tile and, finding no crossing inside it either, returns
+        // its last positive index.
+        int lt = -1;
+        for (int j = 0; j < tpt; ++j) {
+            const int t = tid * tpt + j;
+            if (t < g.nt_all && mine[j] > 0.0f) lt = t;
         }
-        if (tid < rem) {
-            const float tv = tr.elem(nch * E + tid);
-            const float dv = PAIR ? dr.elem(nch * E + tid) : 0.0f;
-            if (wf(tv, dv) > 0.0f) lastpos = nch * E + tid;
-        }
-        return max(block_max_i<NT>(lastpos, sc), 0);
+        cross = block_max_i<NT>(lt, sc);
+        if (cross < 0) return 0;  // no positive weight anywhere
     }
 
     // Pass B: scan inside the crossing tile.

@@ -75,9 +75,12 @@
  *
  * Errors.  Arguments are checked on the host before anything is launched; on
  * an error nothing is written and a negative SV_ERR_* status is returned.
- * Values inside device buffers are not checked: u in [0,1), r in [0,1),
- * logits finite or -inf with at least one finite entry per row (NaN and +inf
- * are undefined).  A draft token outside [0, V) is defined behaviour: it has
+ * Values inside device buffers are not checked: acceptance uniforms u in
+ * [0,1), sampling uniforms r (u_sample, sv_sample's u) in [0,1], logits
+ * finite or -inf with at least one finite entry per row (NaN and +inf are
+ * undefined).  At r = 1 no token's cumulative mass exceeds r, and the draw
+ * returns the last token with positive mass (the rule's own fallback, which
+ * also covers a float32 cumulative sum that rounds below r * total).  A draft token outside [0, V) is defined behaviour: it has
  * probability 0 under both distributions and is rejected (greedy: it never
  * matches).
  */

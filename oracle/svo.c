@@ -44,8 +44,9 @@ static void softmax_row(const void* base, int dtype, int64_t row_off, int V,
 }
 
 /* Inverse-CDF draw from the distribution proportional to w[0..V-1] (w >= 0):
- * the first token whose cumulative normalised mass exceeds r.  If rounding
- * leaves no such token, the last token with positive weight.  Tokens of zero
+ * the first token whose cumulative normalised mass exceeds r.  If no token
+ * qualifies (r = 1, where the total mass 1 does not exceed r, or a sum that
+ * rounds below r), the last token with positive weight.  Tokens of zero
  * weight are never returned.  lo/hi receive the cumulative mass before and
  * through the returned token. */
 static int inverse_cdf(const double* w, int V, double r, double* lo,
