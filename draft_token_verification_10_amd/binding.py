@@ -87,12 +87,20 @@ _workspaces: dict = {}
 
 
 def workspace_for(nbytes: int, device: torch.device, stream: int):
+    """The cached workspace of `stream`, at least `nbytes` long.  It is
+    allocated on `stream` itself, so torch's caching allocator only ever
+    reuses its memory -- or that of the smaller buffer it replaces -- for
+    work ordered after the calls already queued on that stream."""
     if nbytes == 0:
         return None
     key = (device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream == torch.cuda.current_stream(device).cuda_stream:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        else:
+            with torch.cuda.stream(torch.cuda.ExternalStream(stream, device=device)):
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

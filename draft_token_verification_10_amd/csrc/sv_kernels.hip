@@ -1893,10 +1893,13 @@ int launch_tree(const Params& p, int dtype, bool vec, void* stream) {
 int launch_commit(const int32_t* accept_len, const int32_t* tokens, int B, int W,
                   int32_t* seq_len, int32_t* history, long long history_stride, int capacity,
                   int32_t* next_token, long long next_stride, void* stream) {
-    hipLaunchKernelGGL(k_commit, dim3((unsigned)((B + 255) / 256)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), accept_len, tokens, B, W, seq_len,
-                       history, history_stride, capacity, next_token, next_stride);
-    return (int)hipGetLastError();
+    // The launch's own status: an error left by the caller's earlier HIP work
+    // is neither reported here nor cleared.
+    void* args[] = {&accept_len, &tokens, &B, &W, &seq_len, &history, &history_stride,
+                    &capacity, &next_token, &next_stride};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(k_commit),
+                                dim3((unsigned)((B + 255) / 256)), dim3(256), args, 0,
+                                static_cast<hipStream_t>(stream));
 }
 
 }  // namespace sv

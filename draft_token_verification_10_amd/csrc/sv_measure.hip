@@ -73,8 +73,12 @@ extern "C" int sv_stream_read(const void* src, size_t bytes, int blocks, uint32_
     const long long share = (n16 + blocks - 1) / blocks;
     if (share * 16 > kMaxShareBytes - 16) return SV_ERR_SHAPE;
     const long long grid = (n16 + share - 1) / share;  // no empty workgroups
-    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(NT), 0, (hipStream_t)stream,
-                       (const char*)src, n16, share, out);
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+    // The launch's own status (an earlier error of the caller is left alone).
+    const char* s = static_cast<const char*>(src);
+    void* args[] = {&s, const_cast<long long*>(&n16), const_cast<long long*>(&share), &out};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k_stream_read), dim3((unsigned)grid),
+                           dim3(NT), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SV_OK
+               : SV_ERR_HIP;
 }
 #pragma GCC visibility pop

@@ -108,3 +108,93 @@ def test_concurrent_streams_match_serial_calls():
             for outs in g4:
                 for o, e in zip(outs, w):
                     assert torch.equal(o, e), (rep, i)
+
+
+def test_cached_workspace_on_side_stream_with_growing_shapes():
+    """Calls through the binding's cached workspace on a stream that is not
+    torch's current one, each shape needing a larger workspace than the last
+    (so every call drops the buffer the previous one is still using), while
+    the current stream allocates and overwrites buffers of the dropped sizes.
+    The workspace is allocated on the calls' own stream, so none of those
+    buffers can land on memory a queued call still reads: every result equals
+    the same call made alone, and passes the oracle's agreement rules."""
+    from oracle import protocol
+    rng = np.random.default_rng(31)
+    shapes = [(24, 3, 60000), (64, 5, 60000), (128, 8, 60000), (160, 8, 90000)]
+    calls = []
+    for B, k, V in shapes:
+        t64 = rng.standard_normal((B, k + 1, V)) * 3
+        d64 = t64[:, :k] + rng.standard_normal((B, k, V))
+        t, d = W.round_logits(t64, W.BF16), W.round_logits(d64, W.BF16)
+        x = W.gumbel_max(rng, W.as_f64(d, W.BF16), 1.0)
+        ua = W.exact_uniforms(rng, B * k).reshape(B, k)
+        us = W.exact_uniforms(rng, B)
+        dv = [torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16) for a in (t, d)]
+        dv += [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in (x, ua, us)]
+        calls.append(((B, k, V), (t, d, x, ua, us), dv))
+    want = []
+    for (B, k, V), _, (tt, dt, xd, uad, usd) in calls:
+        ws = torch.empty(binding.sv_workspace_bytes(B, 1, k, V), dtype=torch.uint8, device=DEV)
+        dbg = torch.empty((B, k, 2), dtype=torch.float32, device=DEV)
+        a, tok = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, 1.0, dbg_px_qx=dbg,
+                                              workspace=ws)
+        want.append((a.clone(), tok.clone(), dbg.clone()))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        print(f"side-stream workspace growth, round {rep}", flush=True)
+        binding._workspaces.pop((DEV.index, side.cuda_stream), None)
+        side.wait_stream(torch.cuda.current_stream())
+        got, junk = [], []
+        for (B, k, V), _, (tt, dt, xd, uad, usd) in calls:
+            with torch.cuda.stream(side):
+                acc = torch.empty(B, dtype=torch.int32, device=DEV)
+                tok = torch.empty((B, k + 1), dtype=torch.int32, device=DEV)
+                dbg = torch.empty((B, k, 2), dtype=torch.float32, device=DEV)
+            binding.sv_verify_stochastic(tt, dt, xd, uad, usd, 1.0, accept_len=acc, tokens=tok,
+                                         dbg_px_qx=dbg, stream=side.cuda_stream)
+            got.append((acc, tok, dbg))
+            # meanwhile the current stream allocates and overwrites buffers
+            # of the size the call just dropped
+            for nb in (binding.sv_workspace_bytes(B, 1, k, V) // 2,
+                       binding.sv_workspace_bytes(B, 1, k, V)):
+                junk.append(torch.full((max(nb, 1),), 0x7F, dtype=torch.uint8, device=DEV))
+        torch.cuda.synchronize()
+        for i, ((B, k, V), host, _) in enumerate(calls):
+            for o, e in zip(got[i], want[i]):
+                assert torch.equal(o, e), (rep, i)
+            t, d, x, ua, us = host
+            r = protocol.compare_stochastic(t, d, x, ua, us, B=B, k=k, V=V, temperature=1.0,
+                                            accept_len=got[i][0].cpu().numpy(),
+                                            tokens=got[i][1].cpu().numpy(),
+                                            px_qx=got[i][2].cpu().numpy())
+            assert r.ok(), r.summary()
+        del junk
+
+
+def test_launch_status_is_the_launchs_own():
+    """sv_commit and sv_stream_read report their own launch's status: an
+    error that an unrelated HIP call left on this host thread does not turn
+    a good launch into SV_ERR_HIP."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the HIP runtime the library links
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    B, W_ = 8, 3
+    acc = torch.zeros(B, dtype=torch.int32, device=DEV)
+    tok = torch.arange(B * W_, dtype=torch.int32, device=DEV).reshape(B, W_)
+    seq_len = torch.zeros(B, dtype=torch.int32, device=DEV)
+    hist = torch.zeros((B, 16), dtype=torch.int32, device=DEV)
+    nxt = torch.zeros(B, dtype=torch.int32, device=DEV)
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    out = torch.zeros(64, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(1 << 20) != 0  # no such device: an error on this thread
+    binding.sv_commit(acc, tok, seq_len, hist, nxt)  # raises on a non-OK status
+    assert hip.hipSetDevice(1 << 20) != 0
+    binding.sv_stream_read(buf, 64, out)
+    hip.hipGetLastError()
+    torch.cuda.synchronize()
+    assert torch.equal(nxt.cpu(), tok[:, 0].cpu())
+    assert torch.equal(seq_len.cpu(), torch.ones(B, dtype=torch.int32))
