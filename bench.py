@@ -31,6 +31,13 @@ reads).  Every HBM-bound line also carries "achievable_read": the rate of a plai
 read with the same loads (sv_stream_read over 2 GiB) and the path's fraction
 of it, beside the fraction of the 8 TB/s peak.
 
+Order: inputs are generated and placed in HBM, the achievable read rate is
+measured (about 0.2 s of streaming), then W warm-up calls and the K timed
+calls run back to back between two events.  Measuring the read rate first
+also takes the GPU past the dip its clock shows in the first ~20 ms of load
+after idle (per-XCD clock about 2.3 -> 2.06 -> 2.45 GHz), which would
+otherwise fall on the timed calls of the exponential-heavy stochastic kernels.
+
 Inputs smaller than 512 MB are replicated and the copies rotated from call to
 call, so that no call finds its logits in the 256 MB last-level cache (cold
 figures); "warm" repeats the timing on one copy.
@@ -286,11 +293,13 @@ def n_copies(input_bytes: int, forced) -> int:
     return min(MAX_COPIES, math.ceil(COLD_BYTES / max(1, input_bytes)))
 
 
-def cpu_baseline(run, B: int, what: str, min_reps: int = 3, target_s: float = 10.0,
-                 max_s: float = 30.0):
+def cpu_baseline(run, B: int, what: str, nbytes: int, gpu_value: float, min_reps: int = 3,
+                 target_s: float = 10.0, max_s: float = 30.0):
     """The float64 oracle as it stands, on the host cores: whole-batch passes
     repeated until about `target_s` seconds of work (at least `min_reps`
-    passes, never starting one past `max_s`); the median pass is reported."""
+    passes, never starting one past `max_s`); the median pass is reported,
+    with the oracle's rate on the same algorithmic bytes as the GPU figure
+    and the GPU/CPU ratio."""
     from oracle import svo
     times = []
     t_start = time.perf_counter()
@@ -303,10 +312,14 @@ def cpu_baseline(run, B: int, what: str, min_reps: int = 3, target_s: float = 10
             break
     times.sort()
     med = times[len(times) // 2]
-    out = {"value": round(B / med, 2), "unit": "seqs/s", "cores": svo.num_threads(),
+    value = B / med
+    out = {"value": round(value, 2), "unit": "seqs/s", "cores": svo.num_threads(),
            "kind": "oracle",
            "sample": f"all {B} sequences of {what} per pass, {len(times)} passes "
-                     f"({sum(times):.1f} s), median pass {med:.3f} s"}
+                     f"({sum(times):.1f} s), median pass {med:.3f} s",
+           "GBps": round(nbytes / med / 1e9, 3),
+           "gpu_speedup": round(gpu_value / value, 1),
+           "threads": svo.num_threads(), **host_cpu()}
     # the same oracle on one thread: one whole-batch pass
     threads = svo.num_threads()
     svo.set_num_threads(1)
@@ -318,17 +331,21 @@ def cpu_baseline(run, B: int, what: str, min_reps: int = 3, target_s: float = 10
     finally:
         svo.set_num_threads(threads)
     out["single_thread"] = {"value": round(B / one, 2), "unit": "seqs/s", "cores": 1,
+                            "GBps": round(nbytes / one / 1e9, 3),
+                            "gpu_speedup": round(gpu_value / (B / one), 1),
                             "sample": f"one pass over all {B} sequences ({one:.1f} s; "
                                       f"{est:.1f} s expected from the threaded median)"}
     return out
 
 
-def achievable_read(torch, binding, dev, achieved_gbs: float, nbytes: int = 2 << 30,
-                    steps: int = 20) -> dict:
+def achievable_read(torch, binding, dev, nbytes: int = 2 << 30, steps: int = 20) -> dict:
     """The read rate a plain stream with the logit kernels' own loads sustains
     (sv_stream_read: every byte of a 2 GiB buffer, eight times the last-level
     cache, read once by N workgroups each taking one contiguous share), for
-    several N; the best is the practical ceiling reported beside the peak."""
+    several N; the best is the practical ceiling reported beside the peak.
+    Run before the timed steps: its ~0.2 s of streaming also carries the GPU
+    past the clock dip of its first ~20 ms of load after idle, which the
+    exponential-heavy stochastic kernels would otherwise be timed in."""
     buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     out = torch.zeros(4096, dtype=torch.int32, device=dev)
     sweep = {}
@@ -340,8 +357,45 @@ def achievable_read(torch, binding, dev, achieved_gbs: float, nbytes: int = 2 <<
     del buf
     return {"GBps": sweep[best], "frac_of_peak": round(sweep[best] / HBM_PEAK_GBS, 4),
             "workgroups": int(best), "bytes": nbytes, "kernel": "k_stream_read",
-            "GBps_by_workgroups": sweep,
-            "path_frac_of_achievable": round(achieved_gbs / sweep[best], 4)}
+            "GBps_by_workgroups": sweep}
+
+
+def with_path_frac(ach: dict, achieved_gbs: float) -> dict:
+    out = dict(ach)
+    out["path_frac_of_achievable"] = round(achieved_gbs / ach["GBps"], 4)
+    return out
+
+
+def host_cpu() -> dict:
+    """The measuring host: CPU model, logical CPUs, physical cores (distinct
+    (package, core) pairs in /proc/cpuinfo) and the CPUs this process may
+    run on."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                key, _, val = ln.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+    except OSError:
+        pass
+    if phys is not None and core is not None:
+        cores.add((phys, core))
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "physical_cores": len(cores) or None, "cpus_allowed": allowed}
 
 
 def line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_config=None):
@@ -413,6 +467,7 @@ def bench_tree(args, torch, dev, binding, workloads):
     path = torch.empty((B, N), dtype=torch.int32, device=dev)
     fns = [(lambda t=t: binding.sv_verify_greedy_tree(t, x, par, accept_len=acc, tokens=tok,
                                                       path=path)) for t in ts]
+    ach = achievable_read(torch, binding, dev)
     ms, wall = time_calls(fns, args.steps, args.warmup, torch)
     nbytes = tree_bytes(B, N, V, s_b)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -436,12 +491,12 @@ def bench_tree(args, torch, dev, binding, workloads):
         "per_call_us": per_call_us(fns, min(args.steps, 100), torch),
         "mean_accepted_depth": round(float(acc.float().mean().item()), 4),
     }
-    result["achievable_read"] = achievable_read(torch, binding, dev, gbs)
+    result["achievable_read"] = with_path_frac(ach, gbs)
     if not args.no_cpu_baseline:
         from oracle import svo
         result["cpu_baseline"] = cpu_baseline(
             lambda: svo.verify_greedy_tree(tb.target, tb.node_tokens, tb.parents, B=B, N=N, V=V),
-            B, f"the draft-tree batch (B={B}, N={N})")
+            B, f"the draft-tree batch (B={B}, N={N})", nbytes, result["value"])
     print(json.dumps(result), flush=True)
 
 
@@ -632,6 +687,8 @@ def main():
         extra_cfg = {"rows": "target row 0 of every sequence"}
     extra_cfg["input_copies_rotated"] = nc
 
+    print("# achievable read rate (sv_stream_read over 2 GiB)", file=sys.stderr, flush=True)
+    ach = achievable_read(torch, binding, dev)
     print(f"# timing {args.steps} steps after {args.warmup} warmup ({nc} input copies)",
           file=sys.stderr, flush=True)
     ms, wall = time_calls(fns, args.steps, args.warmup, torch)
@@ -668,7 +725,7 @@ def main():
         sides["greedy"] = side(spec, fns_g, gb, kernel_name(spec, mode, greedy=True),
                                f"{traffic_key}_greedy", args, torch)
     result.update(sides)
-    result["achievable_read"] = achievable_read(torch, binding, dev, result["achieved_GBps"])
+    result["achievable_read"] = with_path_frac(ach, result["achieved_GBps"])
 
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
@@ -689,7 +746,7 @@ def main():
                                                        temperature=spec.tau)
         else:
             run = lambda: svo.sample(rows, u, B=B, V=spec.V, temperature=spec.tau)  # noqa
-        result["cpu_baseline"] = cpu_baseline(run, B, what)
+        result["cpu_baseline"] = cpu_baseline(run, B, what, nbytes, result["value"])
     print(json.dumps(result), flush=True)
 
 

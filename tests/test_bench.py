@@ -1,4 +1,5 @@
 """Host-side checks of bench.py's bookkeeping (no GPU)."""
+import os
 import subprocess
 import sys
 
@@ -102,12 +103,20 @@ def test_cpu_baseline_reports_threads_and_single_thread():
     rows = rng.standard_normal((4, 1000)).astype(np.float32)
     u = np.full(4, 0.5, np.float32)
     before = svo.num_threads()
+    nbytes = rows.nbytes + 8 * 4
     out = bench.cpu_baseline(lambda: svo.sample(rows, u, B=4, V=1000), 4, "a tiny batch",
-                             min_reps=3, target_s=0.05)
+                             nbytes, 1e6, min_reps=3, target_s=0.05)
     assert svo.num_threads() == before
     assert out["kind"] == "oracle" and out["cores"] == before and out["value"] > 0
+    assert out["threads"] == before and out["logical_cpus"] == os.cpu_count()
+    assert out["cpu_model"] and out["physical_cores"] >= 1
+    # the oracle's rate on the same bytes, and the GPU's lead over it
+    med = 4 / out["value"]
+    assert abs(out["GBps"] - nbytes / med / 1e9) <= 1e-3 + 1e-3 * out["GBps"]
+    assert abs(out["gpu_speedup"] - 1e6 / out["value"]) <= 0.05 + 1e-3 * out["gpu_speedup"]
     st = out["single_thread"]
     assert st["cores"] == 1 and st["value"] > 0 and st["unit"] == "seqs/s"
+    assert st["GBps"] > 0 and st["gpu_speedup"] > 0
 
 
 def test_fetched_rate():
