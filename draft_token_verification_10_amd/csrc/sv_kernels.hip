@@ -288,25 +288,85 @@ __device__ __forceinline__ void soft_rescale(SoftAcc& a, float newref) {
     a.ref = newref;
 }
 
+// The terms of one step against the reference `ref`, split over two sums.
 template <typename C>
-__device__ __forceinline__ void soft_consume(const C* buf, float c, SoftAcc& a) {
+__device__ __forceinline__ void soft_terms(const C* buf, float c, float ref, float& s0, float& s1) {
     constexpr int E = C::E;
-    float gm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-        for (int e = 0; e < E; ++e) gm = fmaxf(gm, buf[u].get(e));
-    const float gmc = gm * c;
-    if (gmc > a.ref + RESCALE_MARGIN) soft_rescale(a, gmc);
-    const float nref = -a.ref;
+    const float nref = -ref;
+    s0 = fast_exp2(fmaf(buf[0].get(0), c, nref));
+    s1 = E > 1 ? fast_exp2(fmaf(buf[0].get(E > 1 ? 1 : 0), c, nref)) : 0.0f;
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
+            if (u == 0 && e < 2) continue;
             const float t = fast_exp2(fmaf(buf[u].get(e), c, nref));
-            if (e & 1) a.s1 += t;
-            else a.s0 += t;
+            if (e & 1) s1 += t;
+            else s0 += t;
         }
+}
+
+// Add one step of loaded chunks to a thread's normaliser.  The terms are
+// taken against the current reference without first looking for a new
+// maximum: a logit far above the reference shows up as a step sum of at
+// least SUM_GUARD (or inf), and only then is the step redone after raising
+// the reference to the step's maximum.  So every term stays below 2^64 (the
+// sums far inside float range), and the common path spends no instruction
+// on the maximum.  The first step of a thread always takes the slow path
+// (its reference starts at -FLT_MAX, so any finite logit overflows).
+constexpr float SUM_GUARD = 0x1p64f;
+
+template <typename C>
+__device__ __forceinline__ float step_max(const C* buf) {
+    float gm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < C::E; ++e) gm = fmaxf(gm, buf[u].get(e));
+    return gm;
+}
+
+template <typename C>
+__device__ __forceinline__ void soft_consume(const C* buf, float c, SoftAcc& a) {
+    float s0, s1;
+    soft_terms(buf, c, a.ref, s0, s1);
+    if (!(s0 + s1 < SUM_GUARD)) {
+        const float gmc = step_max(buf) * c;
+        if (gmc > a.ref) soft_rescale(a, gmc);
+        soft_terms(buf, c, a.ref, s0, s1);
+    }
+    a.s0 += s0;
+    a.s1 += s1;
+}
+
+// A row's first step: the reference is still -FLT_MAX, so it starts at the
+// step's maximum directly (the guard would always trip here).
+template <typename C>
+__device__ __forceinline__ void soft_consume_first(const C* buf, float c, SoftAcc& a) {
+    const float gmc = step_max(buf) * c;
+    if (gmc > a.ref) soft_rescale(a, gmc);
+    float s0, s1;
+    soft_terms(buf, c, a.ref, s0, s1);
+    a.s0 += s0;
+    a.s1 += s1;
+}
+
+// Step i0 of a row (chunks i0 + tid + u*NT): whole steps load without
+// checks, the row's last step masks chunks past its end with -inf.
+template <int DT, bool VEC, int NT, bool KEEP>
+__device__ __forceinline__ void load_step(const Row<DT, VEC>& row, int i0, Chunk<DT, VEC>* buf) {
+    constexpr int STEP = NT * UNROLL;
+    const int i = i0 + threadIdx.x;
+    if (i0 + STEP <= row.nch) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
+    } else {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (i + u * NT < row.nch) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
+            else buf[u].set_neg_inf();
+        }
+    }
 }
 
 template <int DT, bool VEC, int NT, bool KEEP = false>
@@ -317,19 +377,10 @@ __device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c,
     const int tid = threadIdx.x;
     const int nch = row.nch;
     for (int i0 = 0; i0 < nch; i0 += STEP) {
-        const int i = i0 + tid;
         C buf[UNROLL];
-        if (i0 + STEP <= nch) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
-        } else {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (i + u * NT < nch) buf[u] = row.template chunk_at<KEEP>(i, u * NT);
-                else buf[u].set_neg_inf();
-            }
-        }
-        soft_consume(buf, c, a);
+        load_step<DT, VEC, NT, KEEP>(row, i0, buf);
+        if (i0 == 0) soft_consume_first(buf, c, a);
+        else soft_consume(buf, c, a);
     }
     if (VEC) {
         const int rem = row.n - nch * E;
@@ -643,8 +694,11 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
 // folded into its exponent: p = 2^(t*c - R_t - log2 Z_t).
 struct ResidualW {
     float c, nt, nd;  // nt = -(R_t + log2 Z_t), nd likewise for the draft row
+    // p, q in [0, 1], so p - q clamped to [0, 1] is max(0, p - q): one
+    // subtraction with the output clamp instead of a subtraction and a max
     __device__ __forceinline__ float operator()(float t, float d) const {
-        return fmaxf(fast_exp2(fmaf(t, c, nt)) - fast_exp2(fmaf(d, c, nd)), 0.0f);
+        return __builtin_amdgcn_fmed3f(fast_exp2(fmaf(t, c, nt)) - fast_exp2(fmaf(d, c, nd)),
+                                       0.0f, 1.0f);
     }
 };
 // Unnormalised target weight 2^(t*c - R).
