@@ -133,7 +133,7 @@ def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -
             return "k_greedy_seq"
         if not diagnostics:
             if spec.k >= 6 and spec.B <= 1024:  # capped pass, then the spread continuation
-                return "k_stochastic_seq_exit (capped) + k_exit_stats + k_draw_tiles + k_draw_select"
+                return "k_stochastic_seq_exit (capped) + k_exit_stats + k_draw_tiles"
             return "k_stochastic_seq_exit"
         return "k_stochastic_seq" if uniform else "k_row_stats"
     return "k_row_stats"

@@ -178,8 +178,8 @@ void plan_exit(sv::Params* p, int E, void* workspace, size_t workspace_bytes) {
     w += sv::part_bytes(B, rows, smax);
     p->tilesum = reinterpret_cast<float*>(w);
     w += sv::tilesum_bytes(B);
-    p->meta = reinterpret_cast<int*>(w);
-    w += sv::meta_bytes(B);
+    p->cnt = reinterpret_cast<int*>(w);
+    w += sv::cnt_bytes(B);
     p->xl = reinterpret_cast<float*>(w);
     p->exit_pairs = P;
     p->rows_per_seq = rows;
@@ -233,8 +233,8 @@ int stochastic_impl(const void* target, const void* draft, const int32_t* x, con
         char* w = static_cast<char*>(workspace) + sv::part_bytes(B, pl.rows_per_seq, pl.S);
         p.tilesum = reinterpret_cast<float*>(w);
         w += sv::tilesum_bytes(B);
-        p.meta = reinterpret_cast<int*>(w);
-        w += sv::meta_bytes(B);
+        p.cnt = reinterpret_cast<int*>(w);
+        w += sv::cnt_bytes(B);
         p.xl = reinterpret_cast<float*>(w);
     }
     p.SD = pl.SD;

@@ -169,18 +169,18 @@ inline int plan_exit_pairs(int) { return SV_EXIT_PAIRS; }
 inline size_t exit_flag_bytes(int B) { return round256((size_t)B * 4); }
 
 // Workspace of the row-split layout: float2 statistics [B][rows_per_seq][S],
-// then (stochastic only) tile sums float [B][kMaxTiles + 1], the per
-// sequence draw parameters int4 [B] and the logit at each row's draft token
+// then (stochastic only) tile sums float [B][kMaxTiles + 1], the spread
+// draw's arrival counter int [B] and the logit at each row's draft token
 // float [B][rows_per_seq].
 inline size_t part_bytes(int B, int rows_per_seq, int S) {
     return round256((size_t)B * rows_per_seq * S * 8);
 }
 inline size_t tilesum_bytes(int B) { return round256((size_t)B * (kMaxTiles + 1) * 4); }
-inline size_t meta_bytes(int B) { return round256((size_t)B * 16); }
+inline size_t cnt_bytes(int B) { return round256((size_t)B * 4); }
 inline size_t xl_bytes(int B, int rows_per_seq) { return round256((size_t)B * rows_per_seq * 4); }
 inline size_t workspace_bytes_for(int B, int rows_per_seq, int S, bool stochastic) {
     size_t n = part_bytes(B, rows_per_seq, S);
-    if (stochastic) n += tilesum_bytes(B) + meta_bytes(B) + xl_bytes(B, rows_per_seq);
+    if (stochastic) n += tilesum_bytes(B) + cnt_bytes(B) + xl_bytes(B, rows_per_seq);
     return n;
 }
 
@@ -196,7 +196,7 @@ struct Params {
     float* dbg;
     float* part;          // row-split only: [B][rows_per_seq][S][2]
     float* tilesum;       // row-split stochastic: [B][kMaxTiles + 1]
-    int* meta;            // row-split stochastic: [B][4] draw parameters
+    int* cnt;             // row-split stochastic: [B] arrival counters of the draw groups
     float* xl;            // row-split stochastic: [B][rows_per_seq] logit at the row's draft token
     int SD;               // row-split stochastic: draw workgroups per sequence
     int slice_draw;       // row-split plain sampling (dense, k = 0): draw from slice statistics

@@ -785,6 +785,7 @@ struct StochFin {
     float dl[kMaxK];
     int js;           // slice draw: the chosen slice, the uniform within it,
     float rf, Rm;     // and the row's reference
+    int last;         // spread draw: this group arrived last for its sequence
     float tile_part[(MAX_TILES + 1) * (NT / 64)];
     float tile_excl[MAX_TILES + 1];
 };
@@ -1160,10 +1161,19 @@ __global__ __launch_bounds__(NT) void k_greedy_seq(Params p) {
 // Row-split kernels: statistics per (row, slice), then one finishing
 // workgroup per sequence.
 
+// Zero the spread draw's arrival counters (kernels that run before
+// k_draw_tiles in a call; device-coherent stores, like the counters' updates).
+__device__ __forceinline__ void zero_draw_counters(const Params& p) {
+    if (p.cnt && blockIdx.x == 0)
+        for (int i = threadIdx.x; i < p.B; i += blockDim.x)
+            __hip_atomic_store(p.cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int DT, bool VEC, bool STOCH>
 __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
     __shared__ Scratch<NT_ROW> sc;
     constexpr int NW = NT_ROW / 64;
+    if (STOCH) zero_draw_counters(p);
     const int per_seq = p.rows_per_seq * p.S;
     const int b = blockIdx.x / per_seq;
     const int item = blockIdx.x - b * per_seq;
@@ -1258,7 +1268,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_finish(Params p) {
 // streamed pair have the rest of their rows -- the pairs from
 // min(exit_pairs, k_b) on and the bonus row -- streamed by this persistent
 // row-split kernel, so that a long accepted run is read by many CUs at once
-// instead of one.  Then k_draw_tiles / k_draw_select decide and draw every
+// instead of one.  Then k_draw_tiles decides and draws every
 // sequence from the statistics, spreading each closing-token draw over
 // several workgroups.  p.part is [B][2k+1][p.S] float2; rows are cut into S2
 // <= p.S slices, S2 chosen from the number of still-accepting sequences, and
@@ -1277,15 +1287,21 @@ __device__ __forceinline__ void exit_slicing(const Params& p, int n_active, int 
     S2 = (p.V + slice_len - 1) / slice_len;  // no empty slices; S2 <= s
 }
 
-// Row-split stochastic finish, in two kernels so that the closing-token draw
-// -- one or two full rows per sequence -- is spread over SD workgroups per
-// sequence instead of one:
-//   k_draw_tiles  (B*SD groups): every group merges its sequence's
-//     statistics and takes the decisions itself (cheap, and it saves a
-//     launch), then sums the draw weights over its share of the tiles into
-//     the workspace; group 0 of each sequence writes everything but the
-//     closing token.
-//   k_draw_select (B groups): the tile scan and the scan inside one tile.
+// Row-split stochastic finish in one kernel, k_draw_tiles (B*SD groups), so
+// that the closing-token draw -- one or two full rows per sequence -- is
+// spread over SD workgroups per sequence instead of one: every group merges
+// its sequence's statistics and takes the decisions itself (cheap, and it
+// saves a launch); group 0 writes everything but the closing token; each
+// group sums the draw weights over its share of the tiles and hands the sums
+// over; the last group of the sequence to arrive scans the tile sums and the
+// one tile holding the draw, and writes the token.
+//
+// The hand-over needs no cache writeback or invalidation: the tile sums are
+// written and read with device-coherent (agent-scope atomic, sc1) stores and
+// loads, each thread waits for its stores before the group's barrier, and
+// only then is the sequence's arrival counter raised (relaxed agent-scope
+// atomic).  The counters are zeroed by the statistics kernel that runs
+// before, so a call needs no extra launch to clear them.
 constexpr int NT_DRAW = kDrawRound;
 
 // Group sd of the SD groups that draw sequence b (all threads call).
@@ -1355,14 +1371,7 @@ __device__ void draw_tiles_group(const Params& p, int b, int sd, int SD, StochFi
             if (i < a) out[i] = x[i];
             else if (i > a) out[i] = -1;
         }
-        if (tid == 0) {
-            if (p.accept_len) p.accept_len[b] = a;
-            int* m = p.meta + (size_t)b * 4;
-            m[0] = a;
-            m[1] = __float_as_int(w0);
-            m[2] = __float_as_int(w1);
-            m[3] = __float_as_int(w2);
-        }
+        if (tid == 0 && p.accept_len) p.accept_len[b] = a;
     }
     // this group's tiles of the draw row(s)
     const Row<DT, VEC> tr(stoch_row<DT>(p, sq, a), V);
@@ -1386,13 +1395,47 @@ __device__ void draw_tiles_group(const Params& p, int b, int sd, int SD, StochFi
             cdf_trailing<DT, VEC, false, NT>(tr, dr, w, g, sm.tile_part, t0);
     }
     __syncthreads();
-    float* ts = p.tilesum + (size_t)b * (kMaxTiles + 1);
+    uint32_t* ts = reinterpret_cast<uint32_t*>(p.tilesum) + (size_t)b * (kMaxTiles + 1);
     for (int t = tid; t < t1 - t0; t += NT) {
         float s = 0.0f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) s += sm.tile_part[t * NW + w];
-        ts[t0 + t] = s;
+        __hip_atomic_store(ts + t0 + t, __float_as_uint(s), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
+    // count this group in; the last of the sequence's groups draws the token
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int groups = (g.nt_all + tps - 1) / tps;  // the groups that have tiles
+    if (tid == 0)
+        sm.last = __hip_atomic_fetch_add(p.cnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  groups - 1;
+    __syncthreads();
+    if (!sm.last) return;  // uniform
+    for (int t = tid; t < g.nt_all * NW; t += NT)
+        sm.tile_part[t] = (t % NW) == 0 ? __uint_as_float(__hip_atomic_load(
+                                              ts + t / NW, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                        : 0.0f;
+    __syncthreads();
+    const float rr = p.u_sample[b];
+    float total = 0.0f;
+    int y;
+    if (a < k) {
+        const ResidualW w{c, w0, w1};
+        y = cdf_select<DT, VEC, true, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
+                                          sm.sc);
+        if (!(total > 0.0f)) {
+            // p == q to float precision: the residual is empty; draw from p_a.
+            const TargetW tw{c, w2};
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw, rr,
+                                                    &total, sm.tile_part, sm.tile_excl, sm.sc);
+        }
+    } else {
+        const TargetW w{c, w0};
+        y = cdf_select<DT, VEC, false, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
+                                           sm.sc);
+    }
+    if (tid == 0) p.tokens_out[(size_t)b * (p.k + 1) + a] = y;
 }
 
 template <int DT, bool VEC>
@@ -1488,6 +1531,7 @@ __device__ void exit_stats_groups(const Params& p, int group, int ngroups, ExitS
 template <int DT, bool VEC>
 __global__ __launch_bounds__(NT_ROW) void k_exit_stats(Params p) {
     __shared__ ExitStatsSmem es;
+    zero_draw_counters(p);
     exit_stats_groups<DT, VEC>(p, blockIdx.x, gridDim.x, es);
 }
 
@@ -1539,48 +1583,6 @@ __device__ int slice_draw(const Params& p, const Seq& sq, int b, int r, float u,
     float total;
     return v0 + inverse_cdf_row<DT, VEC, false, NT>(base, nullptr, v1 - v0, tw, sm.rf, &total,
                                                    sm.tile_part, sm.tile_excl, sm.sc);
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(NT_DRAW) void k_draw_select(Params p) {
-    constexpr int NT = NT_DRAW;
-    constexpr int NW = NT / 64;
-    constexpr int E = Chunk<DT, VEC>::E;
-    __shared__ StochFin<NT> sm;
-    const int b = blockIdx.x;
-    if (p.active && p.active[b] == 2) return;  // drawn by the capped pass
-    const Seq sq = seq_of(p, b);
-    const int k = sq.k, V = p.V;
-    const float c = p.c;
-    const float rr = p.u_sample[b];
-    const int* m = p.meta + (size_t)b * 4;
-    const int a = m[0];
-    const float w0 = __int_as_float(m[1]), w1 = __int_as_float(m[2]), w2 = __int_as_float(m[3]);
-    const Row<DT, VEC> tr(stoch_row<DT>(p, sq, a), V);
-    const Row<DT, VEC> dr(stoch_row<DT>(p, sq, a < k ? k + 1 + a : a), V);
-    const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * E : 0);
-    const float* ts = p.tilesum + (size_t)b * (kMaxTiles + 1);
-    for (int t = threadIdx.x; t < g.nt_all * NW; t += NT)
-        sm.tile_part[t] = (t % NW) == 0 ? ts[t / NW] : 0.0f;
-    __syncthreads();
-    float total = 0.0f;
-    int y;
-    if (a < k) {
-        const ResidualW w{c, w0, w1};
-        y = cdf_select<DT, VEC, true, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
-                                          sm.sc);
-        if (!(total > 0.0f)) {
-            // p == q to float precision: the residual is empty; draw from p_a.
-            const TargetW tw{c, w2};
-            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw, rr,
-                                                    &total, sm.tile_part, sm.tile_excl, sm.sc);
-        }
-    } else {
-        const TargetW w{c, w0};
-        y = cdf_select<DT, VEC, false, NT>(tr, dr, w, rr, g, &total, sm.tile_part, sm.tile_excl,
-                                           sm.sc);
-    }
-    if (threadIdx.x == 0) p.tokens_out[(size_t)b * (p.k + 1) + a] = y;
 }
 
 // Plain sampling in one pass, one row per 1024-thread workgroup: while the
@@ -1882,9 +1884,7 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         if (e) return e;
         e = launch1(k_exit_stats<DT, VEC>, p, kExitStatsGrid, NT_ROW, stream);
         if (e) return e;
-        e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
-        if (e) return e;
-        return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);
+        return launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
     }
     if (seq && p.B >= kSeqWideMinB)
         return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
@@ -1901,9 +1901,7 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         return launch1(k_stochastic_finish<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
     if (p.B >= kFinishOneGroupMinB)
         return launch1(k_stochastic_finish<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
-    e = launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
-    if (e) return e;
-    return launch1(k_draw_select<DT, VEC>, p, p.B, NT_DRAW, stream);
+    return launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
 }
 
 template <int DT, bool VEC>

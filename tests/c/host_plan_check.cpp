@@ -80,8 +80,8 @@ static void check_capped_layout(void* ws, size_t bytes, int B, int k) {
     CHECK((const char*)p.active == w);
     CHECK((const char*)p.part == w + sv::exit_flag_bytes(B));
     CHECK((const char*)p.tilesum == (const char*)p.part + sv::part_bytes(B, rows, p.S));
-    CHECK((const char*)p.meta == (const char*)p.tilesum + sv::tilesum_bytes(B));
-    CHECK((const char*)p.xl == (const char*)p.meta + sv::meta_bytes(B));
+    CHECK((const char*)p.cnt == (const char*)p.tilesum + sv::tilesum_bytes(B));
+    CHECK((const char*)p.xl == (const char*)p.cnt + sv::cnt_bytes(B));
     CHECK((const char*)p.xl + sv::xl_bytes(B, rows) <= w + bytes);
     CHECK(p.rows_per_seq == rows);
     CHECK(p.S >= 1 && p.S <= sv::kExitMaxSlices);
