@@ -41,7 +41,8 @@
  *
  * Memory and ownership.  Every pointer is a device pointer owned by the
  * caller (u_accept, u_sample, tokens, outputs and workspace included).  The
- * library allocates nothing and keeps no state between calls.  Logits are
+ * library allocates nothing and keeps no state between calls, apart from the
+ * fixed per-GPU buffer of sv_verify_stochastic_noalloc (below).  Logits are
  * float32 or bfloat16, row-major, one row of V entries every row_stride
  * elements (row_stride >= V; padding entries are never read).  Rows:
  *   stochastic: target row i of sequence b at (b*(k+1) + i) * row_stride,
