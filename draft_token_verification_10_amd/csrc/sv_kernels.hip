@@ -1193,8 +1193,16 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
         // so the finishing kernels need no gather of their own.
         int xi = -1;
         if (p.xl && r != sq.k) xi = p.tokens_in[sq.d0 + (r < sq.k ? r : r - sq.k - 1)];
+        // The rows the closing-token draw most often reads again -- pair 0,
+        // where a rejection most often lands, and the bonus row -- stream
+        // with ordinary loads, so that they are the likeliest to be cached
+        // by then (measured on B=64, k=4, V=128256 bf16: 42.4 against
+        // 43.6 us per call).
         SoftAcc acc;
-        stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
+        if (r == 0 || r == sq.k || r == sq.k + 1)
+            stream_softmax<DT, VEC, NT_ROW, true>(row, p.c, acc);
+        else
+            stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
         float R, Z;
         wave_softmax(acc, R, Z);
         if (lane == 0) {
