@@ -38,6 +38,7 @@ constexpr int NT_SEQ = kSeqThreads;  // sequence-resident workgroup: 16 wave64s
 // 1024-thread groups win).
 constexpr int NT_SEQ_WIDE = kSeqWideThreads;
 constexpr int NT_ROW = 256;    // row-split statistics workgroup: 4 wave64s
+constexpr int NT_ROW_WIDE = 512;  // ... 8 wave64s, for slices of kRowStatsWideChunks chunks or more
 constexpr int NT_FIN = 1024;   // row-split finishing workgroup
 constexpr int UNROLL = 4;      // 16-byte loads in flight per lane while streaming
 constexpr int TUNROLL = 4;     // chunk pairs in flight per lane while sampling
@@ -1169,10 +1170,10 @@ __device__ __forceinline__ void zero_draw_counters(const Params& p) {
             __hip_atomic_store(p.cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int DT, bool VEC, bool STOCH>
-__global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
-    __shared__ Scratch<NT_ROW> sc;
-    constexpr int NW = NT_ROW / 64;
+template <int DT, bool VEC, bool STOCH, int NT>
+__global__ __launch_bounds__(NT) void k_row_stats(Params p) {
+    __shared__ Scratch<NT> sc;
+    constexpr int NW = NT / 64;
     if (STOCH) zero_draw_counters(p);
     const int per_seq = p.rows_per_seq * p.S;
     const int b = blockIdx.x / per_seq;
@@ -1200,9 +1201,9 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
         // 43.6 us per call).
         SoftAcc acc;
         if (r == 0 || r == sq.k || r == sq.k + 1)
-            stream_softmax<DT, VEC, NT_ROW, true>(row, p.c, acc);
+            stream_softmax<DT, VEC, NT, true>(row, p.c, acc);
         else
-            stream_softmax<DT, VEC, NT_ROW>(row, p.c, acc);
+            stream_softmax<DT, VEC, NT>(row, p.c, acc);
         float R, Z;
         wave_softmax(acc, R, Z);
         if (lane == 0) {
@@ -1224,7 +1225,7 @@ __global__ __launch_bounds__(NT_ROW) void k_row_stats(Params p) {
         }
     } else {
         ArgAcc acc;
-        stream_argmax<DT, VEC, NT_ROW>(row, acc);
+        stream_argmax<DT, VEC, NT>(row, acc);
         wave_argmax(acc.best, acc.pos);
         if (lane == 0) {
             sc.f[wave] = acc.best;
@@ -1879,6 +1880,17 @@ static int launch1(K kernel, const Params& p, long long grid, int block, void* s
                                 dim3(block), args, 0, static_cast<hipStream_t>(stream));
 }
 
+// The row-split statistics kernel, in workgroups of NT_ROW_WIDE threads when
+// a slice has kRowStatsWideChunks chunks or more, else NT_ROW.
+template <int DT, bool VEC, bool STOCH>
+static int launch_row_stats(const Params& p, void* stream) {
+    const long long items = (long long)p.B * p.rows_per_seq * p.S;
+    const int chunks = p.slice_len / Chunk<DT, VEC>::E;
+    return chunks >= kRowStatsWideChunks
+               ? launch1(k_row_stats<DT, VEC, STOCH, NT_ROW_WIDE>, p, items, NT_ROW_WIDE, stream)
+               : launch1(k_row_stats<DT, VEC, STOCH, NT_ROW>, p, items, NT_ROW, stream);
+}
+
 template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     if (seq && p.k == 0 && !p.cu)  // plain sampling in one pass
@@ -1901,8 +1913,7 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     if (seq)
         return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream)
                      : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
-    const long long items = (long long)p.B * p.rows_per_seq * p.S;
-    int e = launch1(k_row_stats<DT, VEC, true>, p, items, NT_ROW, stream);
+    int e = launch_row_stats<DT, VEC, true>(p, stream);
     if (e) return e;
     if (p.slice_draw) return launch1(k_sample_draw<DT, VEC>, p, p.B, NT_SAMPLE, stream);
     if (p.B >= kSeqWideMinB)
@@ -1917,8 +1928,7 @@ static int launch_greedy_t(const Params& p, bool seq, void* stream) {
     if (seq && p.B >= kSeqWideMinB)
         return launch1(k_greedy_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
     if (seq) return launch1(k_greedy_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
-    const long long items = (long long)p.B * p.rows_per_seq * p.S;
-    int e = launch1(k_row_stats<DT, VEC, false>, p, items, NT_ROW, stream);
+    int e = launch_row_stats<DT, VEC, false>(p, stream);
     if (e) return e;
     return launch1(k_greedy_finish, p, p.B, NT_FIN, stream);
 }
@@ -1939,8 +1949,7 @@ int launch_greedy(const Params& p, int dtype, bool vec, bool seq, void* stream) 
 
 template <int DT, bool VEC>
 static int launch_tree_t(const Params& p, void* stream) {
-    const long long items = (long long)p.B * p.rows_per_seq * p.S;
-    int e = launch1(k_row_stats<DT, VEC, false>, p, items, NT_ROW, stream);
+    int e = launch_row_stats<DT, VEC, false>(p, stream);
     if (e) return e;
     return launch1(k_tree_finish, p, p.B, NT_FIN, stream);
 }
