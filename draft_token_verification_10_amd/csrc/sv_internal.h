@@ -89,6 +89,9 @@ constexpr int kSampleSliceElems = 16384;
 // Its per-round partial sums sit in registers, which caps a row at
 // kSampleSeqRounds rounds of one chunk per thread.
 constexpr int kSampleSeqRounds = 32;
+// Rows of at most kSampleHeldRounds rounds also keep every chunk they stream
+// in registers, so the draw scans its round without reading it again.
+constexpr int kSampleHeldRounds = 16;
 constexpr long long kSampleSeqBaseElems = 40960;
 constexpr long long kSampleSeqElemsPerRow = 352;
 constexpr int kSampleWideMaxB = 512;

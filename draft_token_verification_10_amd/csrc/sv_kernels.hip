@@ -560,10 +560,19 @@ __device__ __forceinline__ void cdf_trailing(const Row<DT, VEC>& tr, const Row<D
 
 // Scan over tile sums, then pass B.  tile_part must be complete (after a
 // barrier).  *total_out gets the total weight.  All threads call.
-template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
-__device__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const Wt& wf, float r,
+// Where pass B of cdf_select finds the crossing tile's chunks: read from the
+// rows again (the default), or handed over from registers by a caller that
+// kept its own chunk of every round (see k_sample_seq).
+struct ReadAgain {
+    static constexpr bool kHeld = false;
+    template <typename C>
+    __device__ __forceinline__ C round(int) const { return C{}; }
+};
+
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
+__device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const Wt& wf, float r,
                           const TileGeom& g, float* total_out, const float* tile_part,
-                          float* tile_excl, Scratch<NT>& sc) {
+                          float* tile_excl, Scratch<NT>& sc, const Held& held = Held{}) {
     using C = Chunk<DT, VEC>;
     constexpr int E = C::E;
     constexpr int NW = NT / 64;
@@ -642,7 +651,7 @@ __device__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const 
             float wv[E];
             float loc = 0.0f;
             if (ci < nch) {
-                const C tc = tr.chunk(ci);
+                const C tc = Held::kHeld ? held.template round<C>(rd) : tr.chunk(ci);
                 C dc;
                 if (PAIR) dc = dr.chunk(ci);
 #pragma unroll
@@ -1603,11 +1612,54 @@ __device__ int slice_draw(const Params& p, const Seq& sq, int b, int r, float u,
 constexpr int SAMPLE_ROUNDS = kSampleSeqRounds;
 constexpr int SAMPLE_UNROLL = 4;  // rounds loaded per step (SAMPLE_ROUNDS a multiple)
 
-template <int DT, bool VEC, int NT>
+// A thread's chunk of every round of a row, kept in registers: one member
+// per round (no array, which a run-time pick would turn into a scratch
+// buffer), set and picked through compile-time indices.
+template <typename C, int N>
+struct HeldRounds : HeldRounds<C, N - 1> {
+    static constexpr bool kHeld = true;
+    C last;
+    template <int J>
+    __device__ __forceinline__ C& at() {
+        if constexpr (J == N - 1) return last;
+        else return HeldRounds<C, N - 1>::template at<J>();
+    }
+    template <typename C2>
+    __device__ __forceinline__ C2 round(int rd) const {  // rd uniform over the block
+        if (rd == N - 1) return last;
+        return HeldRounds<C, N - 1>::template round<C2>(rd);
+    }
+};
+template <typename C>
+struct HeldRounds<C, 1> {
+    static constexpr bool kHeld = true;
+    C last;
+    template <int J>
+    __device__ __forceinline__ C& at() { return last; }
+    template <typename C2>
+    __device__ __forceinline__ C2 round(int) const { return last; }
+};
+
+// held.at<J>() = buf[J - base] for the rounds J in [base, base + U) (base is
+// a compile-time constant once the caller's loop is unrolled).
+template <int J, int U, typename H, typename C>
+__device__ __forceinline__ void store_held(H& held, int base, const C* buf) {
+    if constexpr (J < kSampleHeldRounds) {
+        if (J >= base && J < base + U) held.template at<J>() = buf[J - base];
+        store_held<J + 1, U>(held, base, buf);
+    }
+}
+
+// HOLD (rows of at most kSampleHeldRounds rounds): every thread also keeps
+// the chunks it streamed, so the round holding the draw is scanned from
+// registers instead of being read again.
+template <int DT, bool VEC, int NT, bool HOLD>
 __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
     using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
     constexpr int E = C::E;
+    constexpr int RMAX = HOLD ? kSampleHeldRounds : SAMPLE_ROUNDS;
+    static_assert(RMAX % SAMPLE_UNROLL == 0, "whole steps");
     __shared__ StochFin<NT> sm;
     __shared__ float wref[NW];
     const int b = blockIdx.x;
@@ -1617,10 +1669,11 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Row<DT, VEC> row(stoch_row<DT>(p, sq, 0), V);
     const TileGeom g = tile_geom<NT>(row.nch, VEC ? V - row.nch * E : 0);
-    float rs[SAMPLE_ROUNDS];  // this thread's sum in each round
+    float rs[RMAX];  // this thread's sum in each round
+    HeldRounds<C, HOLD ? RMAX : 1> held;
     SoftAcc acc;
 #pragma unroll
-    for (int q = 0; q < SAMPLE_ROUNDS / SAMPLE_UNROLL; ++q) {
+    for (int q = 0; q < RMAX / SAMPLE_UNROLL; ++q) {
         if (q * SAMPLE_UNROLL < g.rounds) {  // uniform
             C buf[SAMPLE_UNROLL];
 #pragma unroll
@@ -1651,6 +1704,7 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
                 rs[q * SAMPLE_UNROLL + u] = su;
                 acc.s0 += su;
             }
+            if constexpr (HOLD) store_held<0, SAMPLE_UNROLL>(held, q * SAMPLE_UNROLL, buf);
         } else {
 #pragma unroll
             for (int u = 0; u < SAMPLE_UNROLL; ++u) rs[q * SAMPLE_UNROLL + u] = 0.0f;
@@ -1662,7 +1716,7 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
         if (x * c > acc.ref + RESCALE_MARGIN) {
             const float f = fast_exp2(acc.ref - x * c);
 #pragma unroll
-            for (int j = 0; j < SAMPLE_ROUNDS; ++j) rs[j] *= f;
+            for (int j = 0; j < RMAX; ++j) rs[j] *= f;
             acc.ref = x * c;
         }
         trail = fast_exp2(fmaf(x, c, -acc.ref));
@@ -1678,7 +1732,7 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
     const float f = fast_exp2(acc.ref - R);
     // per-round sums relative to R: the inverse CDF's tiles (one round each)
 #pragma unroll
-    for (int j = 0; j < SAMPLE_ROUNDS; ++j) {
+    for (int j = 0; j < RMAX; ++j) {
         if (j < g.rounds) {  // uniform
             const float w = wave_sum(rs[j] * f);
             if (lane == 0) sm.tile_part[j * NW + wave] = w;
@@ -1691,8 +1745,13 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
     __syncthreads();
     const TargetW tw{c, -R};
     float total;
-    const int y = cdf_select<DT, VEC, false, NT>(row, row, tw, p.u_sample[b], g, &total,
-                                                 sm.tile_part, sm.tile_excl, sm.sc);
+    int y;
+    if constexpr (HOLD)
+        y = cdf_select<DT, VEC, false, NT>(row, row, tw, p.u_sample[b], g, &total, sm.tile_part,
+                                           sm.tile_excl, sm.sc, held);
+    else
+        y = cdf_select<DT, VEC, false, NT>(row, row, tw, p.u_sample[b], g, &total, sm.tile_part,
+                                           sm.tile_excl, sm.sc);
     if (tid == 0) {
         p.tokens_out[b] = y;
         if (p.accept_len) p.accept_len[b] = 0;
@@ -1893,10 +1952,18 @@ static int launch_row_stats(const Params& p, void* stream) {
 
 template <int DT, bool VEC>
 static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
-    if (seq && p.k == 0 && !p.cu)  // plain sampling in one pass
-        return p.B >= kSeqWideMinB
-                   ? launch1(k_sample_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
-                   : launch1(k_sample_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
+    if (seq && p.k == 0 && !p.cu) {  // plain sampling in one pass
+        const int nch = p.V / Chunk<DT, VEC>::E;
+        const bool wide = p.B >= kSeqWideMinB;
+        const bool hold = (nch + (wide ? NT_SEQ_WIDE : NT_SEQ) - 1) / (wide ? NT_SEQ_WIDE : NT_SEQ) <=
+                          kSampleHeldRounds;
+        if (wide)
+            return hold ? launch1(k_sample_seq<DT, VEC, NT_SEQ_WIDE, true>, p, p.B, NT_SEQ_WIDE, stream)
+                        : launch1(k_sample_seq<DT, VEC, NT_SEQ_WIDE, false>, p, p.B, NT_SEQ_WIDE,
+                                  stream);
+        return hold ? launch1(k_sample_seq<DT, VEC, NT_SEQ, true>, p, p.B, NT_SEQ, stream)
+                    : launch1(k_sample_seq<DT, VEC, NT_SEQ, false>, p, p.B, NT_SEQ, stream);
+    }
     if (seq && p.active) {  // capped early exit, then the spread continuation
         const bool wide = p.B >= kSeqWideMinB;
         int e = wide ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)

@@ -497,6 +497,15 @@ SAMPLE_CASES = [
     (300, 65536, W.BF16, 1.0, 0, False, None),
     (512, 98312, W.BF16, 1.0, 0, False, None),
     (400, 16384, W.F32, 1.0, 1, True, "neginf"),
+    # either side of the one-pass sampler's register-held rounds (at most 16
+    # rounds of 1024 chunks, or of 512 beyond 256 rows): held, then read again
+    (256, 131072, W.BF16, 1.0, 0, False, None),
+    (256, 131068, W.BF16, 0.9, 4, False, None),  # 16 rounds plus trailing logits
+    (256, 65540, W.F32, 1.0, 0, False, None),
+    (320, 65536, W.BF16, 1.0, 0, False, None),
+    (320, 65544, W.BF16, 1.0, 0, False, None),
+    (5, 16384, W.F32, 1.0, 0, True, None),
+    (5, 16385, W.BF16, 1.0, 0, True, "neginf"),
 ]
 
 
