@@ -155,8 +155,10 @@ STOCH_CASES = [
     (300, 4, 2053, W.BF16, 1.0, 8, False, "equal"),
     (257, 8, 9, W.F32, 1.0, 0, False, "close"),
     (196, 2, 20011, W.BF16, 1.2, 0, False, "onehot"),
-    # the maximum draft length, both layouts
+    # the maximum draft length, both layouts (the second: 129 rows of 7
+    # slices, more statistics than the draw stages through LDS)
     (3, 64, 1000, W.BF16, 1.0, 0, False, "close"),
+    (2, 64, 32000, W.BF16, 1.0, 0, False, "close"),
     (192, 64, 300, W.F32, 1.0, 0, False, "close"),
     (600, 64, 300, W.F32, 1.0, 0, True, "close"),  # more sequences than CUs
     # extreme temperatures (exponents far from 0 after scaling)
