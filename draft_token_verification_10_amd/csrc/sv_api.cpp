@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <initializer_list>
 
 #include "sv_internal.h"
 
@@ -75,7 +76,8 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
                                          : sv::plan_slices((long long)B * rows_per_seq, V);
     // slice length: a whole number of chunks, then drop empty slices
     const int chunks = (V + E - 1) / E;
-    const int per = (chunks + S0 - 1) / S0;
+    int per = (chunks + S0 - 1) / S0;
+    if (stochastic && !(flags & kPlanSample)) per = sv::draw_aligned_slice(B, V, E, per);
     const int slice_len = per * E;
     const int S = (V + slice_len - 1) / slice_len;
     if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
@@ -101,7 +103,19 @@ int check_workspace(const void* ws, size_t bytes, const Plan& pl) {
 // the load paths: the slice count before rounding to whole chunks).
 size_t rowsplit_need(int B, int rows_per_seq, int V, bool stochastic, bool sample) {
     const long long rows = (long long)B * rows_per_seq;
-    const int S = sample ? sv::plan_slices_sample(rows, V) : sv::plan_slices(rows, V);
+    int S = sample ? sv::plan_slices_sample(rows, V) : sv::plan_slices(rows, V);
+    if (stochastic && !sample) {
+        // or the slices cut to the draw groups' tiles, for any element size
+        // and load path (1, 4 or 8 logits a chunk)
+        const int S0 = S;
+        for (int E : {1, 4, 8}) {
+            const int chunks = (V + E - 1) / E;
+            const int per = sv::draw_aligned_slice(B, V, E, (chunks + S0 - 1) / S0);
+            const long long len = (long long)per * E;
+            const int SE = (int)((V + len - 1) / len);
+            if (SE > S) S = SE;
+        }
+    }
     return sv::workspace_bytes_for(B, rows_per_seq, S, stochastic);
 }
 
