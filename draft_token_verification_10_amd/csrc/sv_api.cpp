@@ -80,7 +80,10 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     if (stochastic && !(flags & kPlanSample)) per = sv::draw_aligned_slice(B, V, E, per);
     const int slice_len = per * E;
     const int S = (V + slice_len - 1) / slice_len;
-    if ((long long)B * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
+    // (sampling from slice statistics pads the statistics grid to whole
+    // groups of 8 rows)
+    const long long Bg = (stochastic && (flags & kPlanSample)) ? (B + 7LL) / 8 * 8 : B;
+    if (Bg * rows_per_seq * S > kMaxGrid) return SV_ERR_SHAPE;
     if (B > kMaxSeqGrid) return SV_ERR_SHAPE;  // finishing kernels: one 1024-thread group per sequence
     pl->S = S;
     pl->slice_len = slice_len;
