@@ -48,7 +48,30 @@ def random_cases(n=160, seed=31):
     return cases
 
 
-@pytest.mark.parametrize("case", random_cases(), ids=lambda c: "{}_{}_B{}_G{}_k{}_V{}_{}_t{}_p{}_u{}".format(
+def small_batch_cases(n=40, seed=37):
+    """Row-split batches (B < 192) over long rows: the spread draw's group
+    count (16 or 8 per sequence), slices cut to its tiles, statistics staged
+    or not, sliced sampling with rows dealt to XCDs."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        mode = ["stochastic", "ragged", "sample", "stochastic"][len(cases) % 4]
+        B = int(np.exp(rng.uniform(0.0, np.log(191.0))))
+        V = int(np.exp(rng.uniform(np.log(2000.0), np.log(300_000.0))))
+        k = int(rng.choice([1, 2, 4, 8, 16]))
+        dtype = int(rng.choice([W.F32, W.BF16]))
+        tau = float(rng.choice([0.7, 1.0]))
+        pad = int(rng.integers(1, 9)) if rng.random() < 0.25 else 0
+        unal = bool(rng.random() < 0.2)
+        rows = B if mode == "sample" else B * (2 * k + 1)
+        if rows * (V + pad) > MAX_ELEMS:
+            continue
+        cases.append((1000 + len(cases), mode, B, 1, k, V, dtype, tau, pad, unal))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_cases() + small_batch_cases(),
+                         ids=lambda c: "{}_{}_B{}_G{}_k{}_V{}_{}_t{}_p{}_u{}".format(
     c[0], c[1], c[2], c[3], c[4], c[5], "bf16" if c[6] else "f32", c[7], c[8], int(c[9])))
 def test_random_shape(case):
     i, mode, B, G, k, V, dtype, tau, pad, unal = case
