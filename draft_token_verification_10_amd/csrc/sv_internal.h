@@ -50,11 +50,12 @@ constexpr int kMaxSlices = 64;
 // The statistics kernel runs 512-thread workgroups on slices of at least
 // kRowStatsWideChunks chunks (16-byte loads, or single logits on the
 // element-wise path), 256-thread ones on shorter slices.  Measured per call
-// (256 / 512 threads): B=64, k=4, V=128256 bf16 (4008 chunks a slice) 41.1 /
-// 40.7 us; B=128, k=8 (16032) 108.1 / 105.8 us; the B=32, G=16, k=4,
-// V=32000 f32 lookahead batch (8000) 54.5 / 53.1 us; but B=16, k=4 (1069)
-// 25.6 / 27.2 us.
-constexpr int kRowStatsWideChunks = 2048;
+// (256 / 512 threads): B=64, k=4, V=128256 bf16 with 4008 chunks a slice
+// 41.1 / 40.7 us, with the draw-aligned 2048 39.7 / 40.3 us; B=128, k=8
+// (16032) 108.1 / 105.8 us; greedy B=128, k=4 (4008) 30.3 / 29.6 us; the
+// B=32, G=16, k=4, V=32000 f32 lookahead batch (8000) 54.5 / 53.1 us; B=16,
+// k=4 (1069) 25.6 / 27.2 us.
+constexpr int kRowStatsWideChunks = 3072;
 
 inline int plan_slices(long long rows, int V) {
     long long s = 1;
