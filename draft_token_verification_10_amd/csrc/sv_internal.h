@@ -132,16 +132,18 @@ inline int draw_tiles(int nch, int rem) {
 }
 
 // The row-split stochastic draw gives every sequence SD workgroups (never
-// more than its tiles): 16 up to 16 sequences, 8 up to 256, 4 beyond.  More
+// more than its tiles): 16 up to 32 sequences, 8 up to 256, 4 beyond.  More
 // groups per sequence shorten each group's share of the re-read but add
 // groups to the hand-over; measured per call on k=4, V=128256 bf16 batches
 // (temporal loads for pair 0 and the bonus row), SD = 16 / 8 / 4:
 //   B=4  22.1 / 24.3 / 28.9 us (63 groups: 22.1);  B=16 25.5 / 26.4 / 31.1
 //   (63: 35.1);  B=32 29.6 / 29.1 / 33.9 (32: 34.8);  B=64 42.4 / 41.1 / 44.2;
 //   at B=128 (k=3) every choice within 0.4 us; in the capped early exit at
-//   B=256, k=8: 115.1 / 109.9 / 111.4 us (2 groups: 114.4).
+//   B=256, k=8: 115.1 / 109.9 / 111.4 us (2 groups: 114.4).  With the slices
+//   cut to the groups' tiles (draw_aligned_slice), 16 / 8: B=24 24.6 / 25.2
+//   us, B=32 27.5 / 27.9 us, B=48 34.2 / 33.9 us, B=64 41.1 / 39.9 us.
 inline int plan_draw_slices(int B, int tiles) {
-    int sd = B <= 16 ? 16 : (B <= 256 ? 8 : 4);
+    int sd = B <= 32 ? 16 : (B <= 256 ? 8 : 4);
     if (sd > tiles) sd = tiles;
     if (sd < 1) sd = 1;
     return sd;
