@@ -51,7 +51,10 @@ struct Plan {
 //   SAMPLE     plain sampling: one pass per row (use_sample_seq()) or
 //              row-split with sliced rows (the draw reads one slice again
 //              instead of the whole row).
-enum PlanFlags { kPlanDefault = 0, kPlanRowSplit = 1, kPlanSample = 2 };
+//   SEQ        the caller forces the sequence-resident layout (stochastic
+//              calls without diagnostics that take the capped early exit
+//              below the usual threshold).
+enum PlanFlags { kPlanDefault = 0, kPlanRowSplit = 1, kPlanSample = 2, kPlanSeq = 4 };
 
 int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dtype,
               bool stochastic, int flags, const void* const* row_bases, int n_bases,
@@ -61,6 +64,7 @@ int make_plan(int B, int G, int rows_per_seq, int V, int64_t row_stride, int dty
     for (int i = 0; i < n_bases; ++i) vec = vec && aligned16(row_bases[i]);
     pl->seq = flags == kPlanDefault && sv::use_seq_resident(B, G);
     if (flags & kPlanSample) pl->seq = sv::use_sample_seq(B, V, vec ? V / (16 / es) : V);
+    if (flags & kPlanSeq) pl->seq = true;
     pl->slice_draw = false;
     pl->rows_per_seq = rows_per_seq;
     pl->vec = vec;
@@ -150,7 +154,7 @@ size_t sv_workspace_bytes(int B, int G, int k, int V) {
     const size_t g = rowsplit_need(B, G * (k + 1), V, false, false);
     // and the capped early exit of dense and ragged stochastic calls, which
     // only sequence-resident batches take
-    if (sv::plan_exit_pairs(k) > 0 && B >= sv::kSeqResidentMinB && B <= sv::kExitMaxB) {
+    if (sv::plan_exit_pairs(k) > 0 && B >= sv::kCappedExitMinB && B <= sv::kExitMaxB) {
         const size_t e = exit_need(B, k, exit_slices_max(V));
         if (e > s) s = e;
     }
@@ -179,14 +183,23 @@ namespace {
 // the first pass at sv::plan_exit_pairs(k) pairs and finish in the row-split
 // layout (see sv_internal.h).  Without a workspace (allowed here) the plain
 // early exit runs, with the same decisions and tokens.
-void plan_exit(sv::Params* p, int E, void* workspace, size_t workspace_bytes) {
-    const int B = p->B, k = p->k, V = p->V;
-    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || B > sv::kExitMaxB) return;
+// Slices per row of the capped early exit's statistics that the workspace
+// holds (at most exit_slices_max(V)), or 0 when the capped exit cannot run
+// (no usable workspace, too many sequences, no capping at this k).
+int capped_exit_slices(int B, int k, int V, const void* workspace, size_t workspace_bytes) {
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0 || B > sv::kExitMaxB) return 0;
     const int P = sv::plan_exit_pairs(k);
-    if (P < 1 || P >= k) return;
+    if (P < 1 || P >= k) return 0;
     int smax = exit_slices_max(V);
     while (smax > 1 && exit_need(B, k, smax) > workspace_bytes) --smax;
-    if (exit_need(B, k, smax) > workspace_bytes) return;
+    return exit_need(B, k, smax) > workspace_bytes ? 0 : smax;
+}
+
+void plan_exit(sv::Params* p, int E, void* workspace, size_t workspace_bytes) {
+    const int B = p->B, k = p->k, V = p->V;
+    const int smax = capped_exit_slices(B, k, V, workspace, workspace_bytes);
+    if (smax == 0) return;
+    const int P = sv::plan_exit_pairs(k);
     const int rows = 2 * k + 1;
     char* w = static_cast<char*>(workspace);
     p->active = reinterpret_cast<int*>(w);
@@ -229,6 +242,11 @@ int stochastic_impl(const void* target, const void* draft, const int32_t* x, con
     // Unequal ragged lengths (known from the total alone) with every row to
     // be read: balance rows, not sequences, over the GPU.
     if (cu && dbg && total_draft < (long long)B * k) flags = kPlanRowSplit;
+    // Without diagnostics, from kCappedExitMinB sequences on: the
+    // sequence-resident layout and its capped early exit (see sv_internal.h).
+    if (flags == kPlanDefault && !dbg && B >= sv::kCappedExitMinB &&
+        !sv::use_seq_resident(B, 1) && capped_exit_slices(B, k, V, workspace, workspace_bytes) > 0)
+        flags = kPlanSeq;
     Plan pl;
     st = make_plan(B, 1, 2 * k + 1, V, row_stride, dtype, true, flags, bases, 2, &pl);
     if (st != SV_OK) return st;

@@ -189,6 +189,17 @@ inline int draw_aligned_slice(int B, int V, int E, int per) {
 // the caller passes a workspace (the plain early exit needs none) and B <=
 // kExitMaxB.
 constexpr int kExitMaxB = 1024;
+// Without diagnostics the capped early exit also runs from kCappedExitMinB
+// sequences on (below kSeqResidentMinB, where the full read is row-split).
+// It reads less only when sequences reject early, so the gain depends on
+// the acceptance rate.  Measured per call, k=8, V=128256 bf16, row-split
+// full read / capped exit: B=96 81.4 / 75.2 us, B=128 104.2 / 80.7 us,
+// B=160 126.8 / 85.3 us on the peaked batch (mean accepted length 1.2);
+// with half the sequences accepting every draft (mean 4-5) B=96 79.5 /
+// 91.9, B=128 102.1 / 96.6, B=160 123.9 / 108.6 us; with every draft
+// accepted B=96 77.7 / 107.6, B=128 99.5 / 124.2, B=160 120.4 / 140.1 us.
+// From 128 sequences on it wins unless nearly every draft is accepted.
+constexpr int kCappedExitMinB = 128;
 constexpr int kExitStatsGrid = 2048;     // persistent statistics groups (8 per CU)
 constexpr long long kExitTargetItems = 2048;
 // A sequence that the capped pass sees rejected at a position below this

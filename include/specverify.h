@@ -142,12 +142,14 @@ extern "C" {
  * (the "early termination" of Novita's verification strategy, read as
  * stopping at the first mismatch); with dbg_px_qx every position of every
  * sequence is evaluated.  The outputs are the same either way.  Given a
- * workspace of sv_workspace_bytes(B, 1, k, V) bytes, batches with 192 <= B
+ * workspace of sv_workspace_bytes(B, 1, k, V) bytes, batches with 128 <= B
  * <= 1024 and k >= 6 use it to keep the few sequences that accept a long run
  * from holding the GPU: each sequence's own workgroup streams at most its
- * first few pairs, and the rows of the sequences still accepting after them
- * are then spread over all compute units (with NULL, 0 the single-workgroup
- * early exit runs instead, with the same decisions and tokens).
+ * first few pairs, stopping at the first rejection, and the rows of the
+ * sequences still accepting after them are then spread over all compute
+ * units (with NULL, 0 the single-workgroup early exit runs instead for
+ * B >= 192, with the same decisions and tokens; below 192 the workspace is
+ * required).
  */
 int sv_verify_stochastic(const void* target_logits, const void* draft_logits,
                          const int32_t* draft_tokens, const float* u_accept,

@@ -128,7 +128,19 @@ int main() {
     CHECK(last.seq && last.p.active == nullptr);
     CHECK(stoch(1025, 8, V, fake(8), sv_workspace_bytes(1025, 1, 8, V), false) == SV_OK);
     CHECK(last.seq && last.p.active == nullptr);
-    CHECK(stoch(191, 8, V, fake(8), sv_workspace_bytes(191, 1, 8, V), false) == SV_OK);
+    // 128..191 sequences without diagnostics (k >= 6, a workspace): the
+    // capped early exit too; with diagnostics, or below 128, row-split
+    for (int B : {128, 160, 191}) {
+        const size_t wsb = sv_workspace_bytes(B, 1, 8, V);
+        CHECK(stoch(B, 8, V, fake(8), wsb, false) == SV_OK);
+        CHECK(last.seq && last.p.active != nullptr);
+        check_capped_layout(fake(8), wsb, B, 8);
+        CHECK(stoch(B, 8, V, fake(8), wsb, true) == SV_OK);
+        CHECK(!last.seq && last.p.active == nullptr);
+        CHECK(stoch(B, 5, V, fake(8), sv_workspace_bytes(B, 1, 5, V), false) == SV_OK);
+        CHECK(!last.seq && last.p.active == nullptr);  // no capping below k = 6
+    }
+    CHECK(stoch(127, 8, V, fake(8), sv_workspace_bytes(127, 1, 8, V), false) == SV_OK);
     CHECK(!last.seq && last.p.active == nullptr);
     // ragged batches take the capped exit too (k_max >= 6, no diagnostics)
     {

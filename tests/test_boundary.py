@@ -93,13 +93,14 @@ def test_workspace_bytes(lib):
     # diagnostics, which may take the row-split layout
     for args in [(192, 1, 8, 128256), (256, 1, 8, 128256), (512, 1, 3, 129280)]:
         assert f(*args) >= args[0] * (2 * args[2] + 1) * 8
-    # ... and, for 192..1024 sequences with k >= 6, the capped early exit: a
+    # ... and, for 128..1024 sequences with k >= 6, the capped early exit: a
     # flag per sequence, statistics for up to 16 slices per row, the draw's
-    # tile sums; no such term for k < 6 or beyond 1024 sequences
-    for B, k in [(192, 6), (256, 8), (1024, 64)]:
+    # tile sums; no such term for k < 6, below 128 or beyond 1024 sequences
+    for B, k in [(128, 8), (160, 6), (192, 6), (256, 8), (1024, 64)]:
         assert f(B, 1, k, 128256) >= B * 4 + B * (2 * k + 1) * 16 * 8 + B * 257 * 4
     assert f(256, 1, 5, 128256) < 256 * 11 * 16 * 8
     assert f(1025, 1, 8, 128256) < 1025 * 17 * 16 * 8
+    assert f(127, 1, 8, 128256) < 127 * 4 + 127 * 17 * 16 * 8 + 127 * 257 * 4
     # bad shapes
     for args in [(-1, 1, 1, 10), (1, 0, 1, 10), (1, 1, -1, 10), (1, 1, 1, 0), (1, 1, 65, 10),
                  (1, 600, 1, 10)]:

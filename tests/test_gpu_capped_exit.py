@@ -1,15 +1,18 @@
 """GPU parity of the capped early exit.
 
-Stochastic calls without diagnostics, with 192..1024 sequences and k >= 6
+Stochastic calls without diagnostics, with 128..1024 sequences and k >= 6
 draft tokens, given a workspace: a first pass streams at most a few pairs per
 sequence (one workgroup each, stopping at the first rejection), the sequences
 that accepted all of them have their remaining rows streamed by a persistent
 row-split kernel, and the row-split draw kernels finish every sequence the
-first pass did not (it draws a rejection at position 0 itself).  The
-same call without a workspace (NULL, 0) takes the plain early exit.  Both are
-checked against the float64 oracle by the stochastic agreement rules, and
-against each other: they must agree wherever the oracle's decisions and CDF
-breakpoints are further than 1e-5 from the uniforms.
+first pass did not (it draws a rejection at position 0 itself).  Each
+capped call is paired with one that reads every row: from 192 sequences on
+the same call without a workspace (NULL, 0), which takes the plain early
+exit; below that, where the full read is row-split and needs the workspace,
+the same call asking for diagnostics.  Both are checked against the float64
+oracle by the stochastic agreement rules, and against each other: they must
+agree wherever the oracle's decisions and CDF breakpoints are further than
+1e-5 from the uniforms.
 """
 import numpy as np
 import pytest
@@ -30,6 +33,17 @@ def _empty():
     return torch.empty(0, dtype=torch.uint8, device=DEV)
 
 
+# Below this many sequences the full read is row-split and needs a workspace.
+SEQ_RESIDENT_MIN_B = 192
+
+
+def _full_read_kw(B, shape):
+    """Arguments that make a stochastic call read every row of the batch."""
+    if B >= SEQ_RESIDENT_MIN_B:
+        return dict(workspace=_empty())
+    return dict(dbg_px_qx=torch.empty(shape, dtype=torch.float32, device=DEV))
+
+
 def _compare(rep_a, rep_b, a1, t1, a2, t2):
     """Capped and plain calls must agree except where either needed a band."""
     if rep_a.decision_band or rep_a.token_band or rep_b.decision_band or rep_b.token_band:
@@ -46,7 +60,8 @@ def run_dense(t, d, x, ua, us, tau, dtype, pad=0, unaligned=False, workspace="de
     xd, uad, usd = dev(x), dev(ua), dev(us)
     ws = None if workspace == "default" else workspace
     a1, t1 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau, workspace=ws)
-    a2, t2 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau, workspace=_empty())
+    a2, t2 = binding.sv_verify_stochastic(tt, dt, xd, uad, usd, tau,
+                                          **_full_read_kw(B, (B, k, 2)))
     torch.cuda.synchronize()
     kw = dict(B=B, k=k, V=V, temperature=tau, row_stride=rs)
     r1 = protocol.compare_stochastic(th, dh, x, ua, us, accept_len=a1.cpu().numpy(),
@@ -62,7 +77,7 @@ CASES = [
     (256, 8, 4103, W.BF16, 1.0, 0, False, "close"),        # most sequences continue
     (256, 8, 2053, W.F32, 1.0, 0, False, "equal"),         # every sequence continues to the bonus
     (256, 8, 2053, W.BF16, 1.0, 0, False, "onehot"),       # nearly all reject at position 0
-    (192, 6, 1000, W.BF16, 0.7, 0, False, "close"),        # k = 6, the smallest batch
+    (192, 6, 1000, W.BF16, 0.7, 0, False, "close"),        # k = 6
     (300, 7, 4103, W.F32, 1.0, 3, False, "close"),         # 512-thread groups, padded rows
     (512, 9, 3001, W.BF16, 1.3, 0, True, "close"),         # element-wise loads
     (1024, 8, 513, W.BF16, 1.0, 0, False, "close"),        # the largest capped batch
@@ -71,6 +86,11 @@ CASES = [
     (256, 8, 2053, W.F32, 1.0, 0, False, "neginf"),
     (256, 8, 2053, W.BF16, 1.0, 0, False, "oov"),
     (192, 8, 32000, W.BF16, 1.0, 0, False, "close"),       # a long row, sliced by the continuation
+    (128, 8, 4103, W.BF16, 1.0, 0, False, "close"),        # the smallest capped batch
+    (160, 8, 2053, W.F32, 1.0, 0, False, None),            # below the full read's own threshold
+    (191, 6, 1000, W.BF16, 0.7, 0, False, "equal"),        # every sequence continues
+    (144, 8, 32000, W.BF16, 1.0, 0, True, "close"),        # element-wise loads, long rows
+    (127, 8, 4103, W.BF16, 1.0, 0, False, "close"),        # one below: row-split, no capping
 ]
 
 
@@ -122,6 +142,8 @@ RAGGED = [
     (256, 8, 4103, W.BF16, 1.0, "mixed"),     # k_b in 0..8: below, at and above 3 pairs
     (300, 6, 2053, W.F32, 0.8, "mixed"),      # k_max = 6, 512-thread groups
     (256, 8, 1000, W.BF16, 1.0, "short"),     # every k_b <= 3: the capped pass finishes all
+    (144, 8, 2053, W.BF16, 1.0, "mixed"),     # the capped exit below the full read's threshold
+    (128, 7, 4103, W.F32, 1.0, "short"),
 ]
 
 
@@ -139,7 +161,7 @@ def test_capped_ragged(case):
     cud, xd, uad, usd = dev(cu), dev(x), dev(ua), dev(us)
     a1, t1 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau)
     a2, t2 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k_max, tau,
-                                                 workspace=_empty())
+                                                 **_full_read_kw(B, (n, 2)))
     torch.cuda.synchronize()
     kw = dict(k_max=k_max, V=V, temperature=tau, row_stride=rs)
     r1 = protocol.compare_stochastic_ragged(th, dh, x, cu, ua, us, accept_len=a1.cpu().numpy(),
@@ -153,13 +175,13 @@ def test_capped_ragged(case):
 
 
 def random_capped_cases(n=24, seed=778):
-    """Seeded shapes on the capped path: 192..1024 sequences, k in 6..16,
+    """Seeded shapes on the capped path: 128..1024 sequences, k in 6..16,
     V from 2000 to 130000 (rows long enough to be sliced by the
     continuation), dense and ragged, padded and unaligned rows."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
-        B = int(rng.integers(192, 1025))
+        B = int(rng.integers(128, 1025))
         k = int(rng.choice([6, 7, 8, 9, 12, 16]))
         V = int(np.exp(rng.uniform(np.log(2000), np.log(130000))))
         while B * (2 * k + 1) * V > 60_000_000:
@@ -190,7 +212,7 @@ def test_capped_random(case):
         cud, xd, uad, usd = dev(cu), dev(x), dev(ua), dev(us)
         o1 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k, tau)
         o2 = binding.sv_verify_stochastic_ragged(tt, dt, xd, cud, uad, usd, k, tau,
-                                                 workspace=_empty())
+                                                 **_full_read_kw(B, (int(cu[-1]), 2)))
         torch.cuda.synchronize()
         a1, t1, a2, t2 = (o.cpu().numpy() for o in (*o1, *o2))
         kw = dict(k_max=k, V=V, temperature=tau, row_stride=rs)
