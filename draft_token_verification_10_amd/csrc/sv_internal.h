@@ -93,6 +93,40 @@ constexpr int kSampleSeqRounds = 32;
 // Rows of at most kSampleHeldRounds rounds also keep every chunk they stream
 // in registers, so the draw scans its round without reading it again.
 constexpr int kSampleHeldRounds = 16;
+// The sequence-resident stochastic kernels keep the row pair they stream
+// last on chip for the closing-token draw, which would otherwise read both
+// rows again: each thread's chunks of the first rounds of the target row in
+// registers (4 VGPRs per round for 16-byte chunks), and as many rounds of
+// the draft row as fit in the LDS left beside the kernel's own
+// (kLdsBytesPerCu per CU).  Rounds held, per kernel and workgroup size: as
+// many as fit in the 128 VGPRs that four waves per SIMD allow without
+// spilling, except where holding measured no gain (the early exit with
+// 512-thread groups, two or more per CU: 136.8 against 137.5 us on B=512,
+// k=3, V=129280 bf16).  Measured per call, V=128256 bf16: full read B=256,
+// k=8 186.7 -> 186.4 us, B=512 k=3 (V=129280) 171.6 -> 170.5 us, B=1024 k=3
+// 340.5 -> 335.5 us; capped early exit B=256 k=8 108.8 -> 104.5 us.
+#ifndef SV_HOLD_SEQ_1024
+#define SV_HOLD_SEQ_1024 12
+#endif
+#ifndef SV_HOLD_SEQ_512
+#define SV_HOLD_SEQ_512 16
+#endif
+#ifndef SV_HOLD_EXIT_1024
+#define SV_HOLD_EXIT_1024 12
+#endif
+#ifndef SV_HOLD_EXIT_512
+#define SV_HOLD_EXIT_512 0
+#endif
+constexpr int kPairHeldRounds = 16;  // the most any kernel holds
+// Holding limits the full read to two 512-thread workgroups per CU (LDS and
+// registers), where up to four fit otherwise: beyond kSeqWideHoldMaxB
+// sequences (two per CU) a second round of workgroups would follow, so
+// nothing is held there (B=700, k=8, V=32000 bf16: 132.6 us without, 161.1
+// with; B=1024, k=3, V=128256: 339.4 without, 334.5 with, two full rounds).
+constexpr int kSeqWideHoldMaxB = 512;
+constexpr int held_rounds_seq(int nt) { return nt >= 1024 ? SV_HOLD_SEQ_1024 : SV_HOLD_SEQ_512; }
+constexpr int held_rounds_exit(int nt) { return nt >= 1024 ? SV_HOLD_EXIT_1024 : SV_HOLD_EXIT_512; }
+constexpr size_t kLdsBytesPerCu = 160 * 1024;
 constexpr long long kSampleSeqBaseElems = 40960;
 constexpr long long kSampleSeqElemsPerRow = 352;
 constexpr int kSampleWideMaxB = 512;
@@ -204,6 +238,9 @@ constexpr int kExitStatsGrid = 2048;     // persistent statistics groups (8 per 
 constexpr long long kExitTargetItems = 2048;
 // A sequence that the capped pass sees rejected at a position below this
 // draws its token in that pass (its CU is free long before the pass ends).
+// Measured with the rejected pair held on chip, B=256, k=8, V=128256 bf16:
+// 104.5 us drawing after a rejection at position 0 only, 108.2 after
+// positions 0 and 1, 116.6 after any of the three capped pairs.
 #ifndef SV_EXIT_DRAW_HERE
 constexpr int kExitDrawHere = 1;
 #else

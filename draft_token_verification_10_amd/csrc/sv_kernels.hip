@@ -274,6 +274,96 @@ __device__ __forceinline__ int block_max_i(int v, Scratch<NT>& sc) {
 }
 
 // ------------------------------------------------------------------------
+// A thread's chunk of rounds 0..N-1 of a row, kept in registers: one member
+// per round (no array, which a run-time pick would turn into a scratch
+// buffer), set and picked through compile-time indices.  round() also takes
+// a run-time round (uniform over the block): it selects among the values of
+// every held round without branches, since branches that each read another
+// member merge into a read through a pointer picked at run time, which
+// keeps the whole object in scratch memory.
+template <typename C, int N>
+struct HeldRounds : HeldRounds<C, N - 1> {
+    static constexpr bool kHeld = true;
+    static constexpr int kRounds = N;
+    C last;
+    template <int J>
+    __device__ __forceinline__ C& at() {
+        if constexpr (J == N - 1) return last;
+        else return HeldRounds<C, N - 1>::template at<J>();
+    }
+    __device__ __forceinline__ C round(int rd) const {
+        C v = HeldRounds<C, N - 1>::round(rd);
+        const bool hit = rd == N - 1;
+#pragma unroll
+        for (int w = 0; w < (int)(sizeof(v.w) / sizeof(v.w[0])); ++w) v.w[w] = hit ? last.w[w] : v.w[w];
+        return v;
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ C tchunk(const R& tr, int rd) const {
+        return rd < N ? round(rd) : tr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ C dchunk(const R& dr, int rd) const {
+        return dr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const { return dr.elem(v); }
+};
+template <typename C>
+struct HeldRounds<C, 1> {
+    static constexpr bool kHeld = true;
+    static constexpr int kRounds = 1;
+    C last;
+    template <int J>
+    __device__ __forceinline__ C& at() { return last; }
+    __device__ __forceinline__ C round(int) const { return last; }
+    template <int NT, typename R>
+    __device__ __forceinline__ C tchunk(const R& tr, int rd) const {
+        return rd < 1 ? last : tr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ C dchunk(const R& dr, int rd) const {
+        return dr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const { return dr.elem(v); }
+};
+
+// No round held: everything is read again.
+template <typename C>
+struct HeldRounds<C, 0> {
+    static constexpr bool kHeld = true;
+    static constexpr int kRounds = 0;
+    __device__ __forceinline__ C round(int) const { return C{}; }
+    template <int NT, typename R>
+    __device__ __forceinline__ C tchunk(const R& tr, int rd) const {
+        return tr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ C dchunk(const R& dr, int rd) const {
+        return dr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const { return dr.elem(v); }
+};
+
+// held.at<J>() = buf[J - base] for the rounds J < N in [base, base + U)
+// (base is a compile-time constant once the caller's loop is unrolled).
+template <int J, int N, int U, typename H, typename C>
+__device__ __forceinline__ void store_held(H& held, int base, const C* buf) {
+    if constexpr (J < N) {
+        if (J >= base && J < base + U) held.template at<J>() = buf[J - base];
+        store_held<J + 1, N, U>(held, base, buf);
+    }
+}
+
+// ------------------------------------------------------------------------
 // Streaming reductions of one row, per thread.  Thread t visits chunks
 // t, t+NT, t+2NT, ... in increasing order, UNROLL loads in flight.
 
@@ -370,12 +460,24 @@ __device__ __forceinline__ void load_step(const Row<DT, VEC>& row, int i0, Chunk
     }
 }
 
+// The row's last n % E logits (vector rows), one per thread.
+template <int DT, bool VEC>
+__device__ __forceinline__ void soft_trailing(const Row<DT, VEC>& row, float c, SoftAcc& a) {
+    if (VEC) {
+        constexpr int E = Chunk<DT, VEC>::E;
+        const int rem = row.n - row.nch * E;
+        if ((int)threadIdx.x < rem) {
+            const float x = row.elem(row.nch * E + threadIdx.x);
+            if (x * c > a.ref + RESCALE_MARGIN) soft_rescale(a, x * c);
+            a.s0 += fast_exp2(fmaf(x, c, -a.ref));
+        }
+    }
+}
+
 template <int DT, bool VEC, int NT, bool KEEP = false>
 __device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c, SoftAcc& a) {
     using C = Chunk<DT, VEC>;
-    constexpr int E = C::E;
     constexpr int STEP = NT * UNROLL;
-    const int tid = threadIdx.x;
     const int nch = row.nch;
     for (int i0 = 0; i0 < nch; i0 += STEP) {
         C buf[UNROLL];
@@ -383,14 +485,62 @@ __device__ __forceinline__ void stream_softmax(const Row<DT, VEC>& row, float c,
         if (i0 == 0) soft_consume_first(buf, c, a);
         else soft_consume(buf, c, a);
     }
-    if (VEC) {
-        const int rem = row.n - nch * E;
-        if (tid < rem) {
-            const float x = row.elem(nch * E + tid);
-            if (x * c > a.ref + RESCALE_MARGIN) soft_rescale(a, x * c);
-            a.s0 += fast_exp2(fmaf(x, c, -a.ref));
+    soft_trailing(row, c, a);
+}
+
+// stream_softmax that also keeps this thread's chunk of rounds 0..N-1 in
+// registers (held.at<J>(); chunks past the row's end hold -inf): the first
+// N / UNROLL steps are unrolled so that every round has its own register.
+// Every held round is written, so nothing held before stays live.
+template <int DT, bool VEC, int NT, bool KEEP, int N>
+__device__ __forceinline__ void stream_softmax_hold(const Row<DT, VEC>& row, float c, SoftAcc& a,
+                                                    HeldRounds<Chunk<DT, VEC>, N>& held) {
+    using C = Chunk<DT, VEC>;
+    static_assert(N % UNROLL == 0, "whole steps");
+    constexpr int STEP = NT * UNROLL;
+    const int nch = row.nch;
+#pragma unroll
+    for (int q = 0; q < N / UNROLL; ++q) {
+        C buf[UNROLL];
+        if (q * STEP < nch) {  // uniform
+            load_step<DT, VEC, NT, KEEP>(row, q * STEP, buf);
+            if (q == 0) soft_consume_first(buf, c, a);
+            else soft_consume(buf, c, a);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) buf[u].set_neg_inf();
+        }
+        store_held<0, N, UNROLL>(held, q * UNROLL, buf);
+    }
+    for (int i0 = N * NT; i0 < nch; i0 += STEP) {
+        C buf[UNROLL];
+        load_step<DT, VEC, NT, KEEP>(row, i0, buf);
+        soft_consume(buf, c, a);
+    }
+    soft_trailing(row, c, a);
+}
+
+// stream_softmax that also stores this thread's chunk of rounds 0..lr-1 in
+// LDS (stash[rd * NT + tid]; chunks past the row's end hold -inf).
+template <int DT, bool VEC, int NT, bool KEEP = false>
+__device__ __forceinline__ void stream_softmax_stash(const Row<DT, VEC>& row, float c, SoftAcc& a,
+                                                     Chunk<DT, VEC>* stash, int lr) {
+    using C = Chunk<DT, VEC>;
+    constexpr int STEP = NT * UNROLL;
+    const int nch = row.nch;
+    for (int i0 = 0; i0 < nch; i0 += STEP) {
+        C buf[UNROLL];
+        load_step<DT, VEC, NT, KEEP>(row, i0, buf);
+        if (i0 == 0) soft_consume_first(buf, c, a);
+        else soft_consume(buf, c, a);
+        const int r0 = i0 / NT;
+        if (r0 < lr) {  // uniform
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (r0 + u < lr) stash[(r0 + u) * NT + threadIdx.x] = buf[u];
         }
     }
+    soft_trailing(row, c, a);
 }
 
 // Merge a wave's softmax normalisers into (R, Z) (valid in every lane).
@@ -499,12 +649,56 @@ __device__ __forceinline__ float chunk_weight_sum(const Wt& wf, const C& t, cons
     return acc;
 }
 
+// Where the draw finds a round's chunks (round rd, chunk ci = rd * NT + tid
+// of this thread) and the trailing logits (element v): read from the rows
+// again (the default), or kept on chip by the kernel that streamed them
+// (HeldRounds, PairHold).
+struct ReadAgain {
+    static constexpr bool kHeld = false;
+    template <int NT, typename R>
+    __device__ __forceinline__ auto tchunk(const R& tr, int rd) const {
+        return tr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ auto dchunk(const R& dr, int rd) const {
+        return dr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const { return dr.elem(v); }
+};
+// Read again, with the draft side switched off at run time (every draft
+// logit -inf, nothing loaded), for draws with a DrawW weight.
+struct ReadPair {
+    static constexpr bool kHeld = false;
+    bool dlive = true;
+    template <int NT, typename R>
+    __device__ __forceinline__ auto tchunk(const R& tr, int rd) const {
+        return tr.chunk_at(threadIdx.x, rd * NT);
+    }
+    template <int NT, typename R>
+    __device__ __forceinline__ auto dchunk(const R& dr, int rd) const {
+        decltype(dr.chunk(0)) c;
+        if (dlive) c = dr.chunk_at(threadIdx.x, rd * NT);
+        else c.set_neg_inf();
+        return c;
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const {
+        return dlive ? dr.elem(v) : -INFINITY;
+    }
+};
+
 // Pass A over the block-wide rounds [r_begin, r_end) (no barriers;
 // tile_part pre-zeroed; tile t is stored at slot (t - tile_base) * NW).
-template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
 __device__ __forceinline__ void cdf_pass_a_rounds(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
                                                   const Wt& wf, const TileGeom& g, int r_begin,
-                                                  int r_end, int tile_base, float* tile_part) {
+                                                  int r_end, int tile_base, float* tile_part,
+                                                  const Held& held = Held{}) {
     using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -514,8 +708,8 @@ __device__ __forceinline__ void cdf_pass_a_rounds(const Row<DT, VEC>& tr, const 
         for (int u = 0; u < TUNROLL; ++u) {
             const int ci = (r0 + u) * NT + tid;
             if (ci < g.nch) {
-                tb[u] = tr.chunk(ci);
-                if (PAIR) db[u] = dr.chunk(ci);
+                tb[u] = held.template tchunk<NT>(tr, r0 + u);
+                if (PAIR) db[u] = held.template dchunk<NT>(dr, r0 + u);
             } else {
                 tb[u].set_neg_inf();
                 if (PAIR) db[u].set_neg_inf();
@@ -539,10 +733,10 @@ __device__ __forceinline__ void cdf_pass_a_rounds(const Row<DT, VEC>& tr, const 
 // the capped early exit 110.3 -> 109.5 us).  Each tile is one round here
 // unless a row has more than MAX_TILES rounds; the tile sums are the same
 // sums either way, in a different order only for such rows.
-template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
 __device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
                                                  const Wt& wf, const TileGeom& g,
-                                                 float* tile_part) {
+                                                 float* tile_part, const Held& held = Held{}) {
     using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -554,8 +748,8 @@ __device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const R
             const int round = r0 + u;
             const int ci = round * NT + tid;
             if (round >= 0 && ci < g.nch) {
-                tb[u] = tr.chunk(ci);
-                if (PAIR) db[u] = dr.chunk(ci);
+                tb[u] = held.template tchunk<NT>(tr, round);
+                if (PAIR) db[u] = held.template dchunk<NT>(dr, round);
             } else {
                 tb[u].set_neg_inf();
                 if (PAIR) db[u].set_neg_inf();
@@ -573,34 +767,69 @@ __device__ __forceinline__ void cdf_pass_a_block(const Row<DT, VEC>& tr, const R
 }
 
 // The trailing-logits tile (no barriers; tile_part pre-zeroed).
-template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
 __device__ __forceinline__ void cdf_trailing(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr,
                                              const Wt& wf, const TileGeom& g, float* tile_part,
-                                             int tile_base = 0) {
+                                             int tile_base = 0, const Held& held = Held{}) {
     constexpr int NW = NT / 64;
     constexpr int E = Chunk<DT, VEC>::E;
     if (g.rem == 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float w = 0.0f;
     if (tid < g.rem) {
-        const float tv = tr.elem(g.nch * E + tid);
-        const float dv = PAIR ? dr.elem(g.nch * E + tid) : 0.0f;
+        const float tv = held.telem(tr, g.nch * E + tid);
+        const float dv = PAIR ? held.delem(dr, g.nch * E + tid) : 0.0f;
         w = wf(tv, dv);
     }
     w = wave_sum(w);
     if (lane == 0) tile_part[(g.ntiles - tile_base) * NW + wave] += w;
 }
 
+// The row pair a sequence-resident kernel streamed last, kept on chip for
+// the closing-token draw (whose residual weights need both rows again once
+// their normalisers are known): this thread's chunks of target rounds
+// 0..N-1 in registers, and draft rounds 0..lr-1 in LDS (the chunk of round
+// rd for thread tid at stash[rd * NT + tid]).  Later rounds are read again.
+// dlive false: the draft side is switched off (as in ReadPair).
+template <typename C, int N, int NT>
+struct PairHold {
+    static constexpr bool kHeld = true;
+    static constexpr int kRounds = N;
+    HeldRounds<C, N> t;
+    C* stash;
+    int lr;
+    bool dlive;
+    template <int, typename R>  // the block size is NT
+    __device__ __forceinline__ C tchunk(const R& tr, int rd) const {
+        return t.template tchunk<NT>(tr, rd);
+    }
+    template <int, typename R>
+    __device__ __forceinline__ C dchunk(const R& dr, int rd) const {
+        C c;
+        if (!dlive) c.set_neg_inf();
+        else if (rd < lr) c = stash[rd * NT + threadIdx.x];
+        else c = dr.chunk_at(threadIdx.x, rd * NT);
+        return c;
+    }
+    template <typename R>
+    __device__ __forceinline__ float telem(const R& tr, int v) const { return tr.elem(v); }
+    template <typename R>
+    __device__ __forceinline__ float delem(const R& dr, int v) const {
+        return dlive ? dr.elem(v) : -INFINITY;
+    }
+};
+// The memory side of a held row (pair): what is not held is read again.
+template <typename C, int N, int NT>
+__device__ __forceinline__ ReadPair read_again_of(const PairHold<C, N, NT>& h) {
+    ReadPair r;
+    r.dlive = h.dlive;
+    return r;
+}
+template <typename C, int N>
+__device__ __forceinline__ ReadAgain read_again_of(const HeldRounds<C, N>&) { return ReadAgain{}; }
+
 // Scan over tile sums, then pass B.  tile_part must be complete (after a
 // barrier).  *total_out gets the total weight.  All threads call.
-// Where pass B of cdf_select finds the crossing tile's chunks: read from the
-// rows again (the default), or handed over from registers by a caller that
-// kept its own chunk of every round (see k_sample_seq).
-struct ReadAgain {
-    static constexpr bool kHeld = false;
-    template <typename C>
-    __device__ __forceinline__ C round(int) const { return C{}; }
-};
 
 template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
 __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, VEC>& dr, const Wt& wf, float r,
@@ -669,8 +898,8 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
     if (cross == g.ntiles) {  // the trailing-logits tile
         float w = 0.0f;
         if (tid < rem) {
-            const float tv = tr.elem(nch * E + tid);
-            const float dv = PAIR ? dr.elem(nch * E + tid) : 0.0f;
+            const float tv = held.telem(tr, nch * E + tid);
+            const float dv = PAIR ? held.delem(dr, nch * E + tid) : 0.0f;
             w = wf(tv, dv);
             if (w > 0.0f) tile_last = nch * E + tid;
         }
@@ -684,9 +913,9 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
             float wv[E];
             float loc = 0.0f;
             if (ci < nch) {
-                const C tc = Held::kHeld ? held.template round<C>(rd) : tr.chunk(ci);
+                const C tc = held.template tchunk<NT>(tr, rd);
                 C dc;
-                if (PAIR) dc = dr.chunk(ci);
+                if (PAIR) dc = held.template dchunk<NT>(dr, rd);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     wv[e] = PAIR ? wf(tc.get(e), dc.get(e)) : wf(tc.get(e), 0.0f);
@@ -716,10 +945,10 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
 }
 
 // The whole draw in one call.  All threads call.
-template <int DT, bool VEC, bool PAIR, int NT, typename Wt>
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename Held = ReadAgain>
 __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const Wt& wf, float r,
                                float* total_out, float* tile_part, float* tile_excl,
-                               Scratch<NT>& sc) {
+                               Scratch<NT>& sc, const Held& held = Held{}) {
     constexpr int NW = NT / 64;
     const Row<DT, VEC> tr(trow, V);
     const Row<DT, VEC> dr(PAIR ? drow : trow, V);
@@ -727,10 +956,65 @@ __device__ int inverse_cdf_row(const char* trow, const char* drow, int V, const 
     const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * Chunk<DT, VEC>::E : 0);
     for (int t = tid; t < g.nt_all * NW; t += NT) tile_part[t] = 0.0f;
     __syncthreads();
-    cdf_pass_a_block<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part);
-    cdf_trailing<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part);
+    cdf_pass_a_block<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part, held);
+    cdf_trailing<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part, 0, held);
     __syncthreads();
-    return cdf_select<DT, VEC, PAIR, NT>(tr, dr, wf, r, g, total_out, tile_part, tile_excl, sc);
+    return cdf_select<DT, VEC, PAIR, NT>(tr, dr, wf, r, g, total_out, tile_part, tile_excl, sc,
+                                         held);
+}
+
+// inverse_cdf_row for a row (pair) the caller kept on chip (PairHold, or
+// HeldRounds for a single row): pass A reads the rounds beyond the held
+// ones from memory first, then sums the held rounds (their loads, if any,
+// from LDS); pass B scans the crossing tile's chunks from where they are.
+// The tile sums are the same sums as inverse_cdf_row's.  All threads call.
+template <int DT, bool VEC, bool PAIR, int NT, typename Wt, typename H>
+__device__ __forceinline__ int inverse_cdf_held(const char* trow, const char* drow, int V, const Wt& wf, float r,
+                                float* total_out, float* tile_part, float* tile_excl,
+                                Scratch<NT>& sc, const H& hold) {
+    using C = Chunk<DT, VEC>;
+    constexpr int NW = NT / 64;
+    constexpr int N = H::kRounds;
+    static_assert(N % TUNROLL == 0, "whole steps");
+    const Row<DT, VEC> tr(trow, V);
+    const Row<DT, VEC> dr(PAIR ? drow : trow, V);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const TileGeom g = tile_geom<NT>(tr.nch, VEC ? V - tr.nch * C::E : 0);
+    for (int t = tid; t < g.nt_all * NW; t += NT) tile_part[t] = 0.0f;
+    __syncthreads();
+    if (g.rounds > N)
+        cdf_pass_a_rounds<DT, VEC, PAIR, NT>(tr, dr, wf, g, N, g.rounds, 0, tile_part,
+                                             read_again_of(hold));
+#pragma unroll
+    for (int r0 = 0; r0 < N; r0 += TUNROLL) {
+        if (r0 < g.rounds) {  // uniform
+            C tb[TUNROLL], db[TUNROLL];
+#pragma unroll
+            for (int u = 0; u < TUNROLL; ++u) {
+                const int rd = r0 + u;
+                const int ci = rd * NT + tid;
+                if (ci < g.nch) {
+                    tb[u] = hold.template tchunk<NT>(tr, rd);
+                    if (PAIR) db[u] = hold.template dchunk<NT>(dr, rd);
+                } else {
+                    tb[u].set_neg_inf();
+                    if (PAIR) db[u].set_neg_inf();
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TUNROLL; ++u) {
+                const int round = r0 + u;
+                if (round < g.rounds) {  // uniform
+                    const float acc = wave_sum(chunk_weight_sum<PAIR>(wf, tb[u], db[u]));
+                    if (lane == 0) tile_part[(round / g.m) * NW + wave] += acc;
+                }
+            }
+        }
+    }
+    cdf_trailing<DT, VEC, PAIR, NT>(tr, dr, wf, g, tile_part, 0, read_again_of(hold));
+    __syncthreads();
+    return cdf_select<DT, VEC, PAIR, NT>(tr, dr, wf, r, g, total_out, tile_part, tile_excl, sc,
+                                         hold);
 }
 
 // Residual weight max(0, p - q) of one row pair, with each normaliser
@@ -742,6 +1026,20 @@ struct ResidualW {
     __device__ __forceinline__ float operator()(float t, float d) const {
         return __builtin_amdgcn_fmed3f(fast_exp2(fmaf(t, c, nt)) - fast_exp2(fmaf(d, c, nd)),
                                        0.0f, 1.0f);
+    }
+};
+// Either weight, chosen at run time (uniform), so that one copy of the held
+// draw serves both the residual and the bonus token (each copy of a draw
+// over held registers costs registers of its own): pair, max(0, p - q) as
+// ResidualW; otherwise 2^(t*c + nt), as TargetW with nt = -R (the draft
+// side then reads as -inf and is never loaded).  Each gives exactly the
+// value of the weight it stands for.
+struct DrawW {
+    float c, nt, nd;
+    bool pair;
+    __device__ __forceinline__ float operator()(float t, float d) const {
+        const float pt = fast_exp2(fmaf(t, c, nt));
+        return pair ? __builtin_amdgcn_fmed3f(pt - fast_exp2(fmaf(d, c, nd)), 0.0f, 1.0f) : pt;
     }
 };
 // Unnormalised target weight 2^(t*c - R).
@@ -834,8 +1132,11 @@ struct StochFin {
 };
 
 // Needs R[], Z[] of every row of sequence b in LDS (after a barrier).
-template <int DT, bool VEC, int NT>
-__device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin<NT>& sm) {
+// hold (a PairHold, or ReadAgain for none): pair 0 (target row 0 alone when
+// k = 0) kept on chip.
+template <int DT, bool VEC, int NT, typename H>
+__device__ __forceinline__ void finish_stochastic(const Params& p, int b, const Seq& s,
+                                                  StochFin<NT>& sm, H& hold) {
     const int tid = threadIdx.x;
     const int k = s.k, V = p.V;
     const int32_t* x = p.tokens_in + s.d0;
@@ -877,24 +1178,50 @@ __device__ void finish_stochastic(const Params& p, int b, const Seq& s, StochFin
     }
     const float rr = p.u_sample[b];
     const char* trow = stoch_row<DT>(p, s, a);
-    float total;
-    int y;
-    if (a < k) {
-        const char* drow = stoch_row<DT>(p, s, k + 1 + a);
-        const ResidualW w{p.c, -(sm.R[a] + __log2f(sm.Z[a])),
-                          -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a]))};
-        y = inverse_cdf_row<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.tile_part,
-                                               sm.tile_excl, sm.sc);
-        if (!(total > 0.0f)) {
-            // p == q to float precision: the residual is empty; draw from p_a.
-            const TargetW tw{p.c, -sm.R[a]};
-            y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
-                                                    sm.tile_excl, sm.sc);
+    float total = 0.0f;
+    int y = 0;
+    bool read_again = true;
+    if constexpr (H::kHeld) {
+        if (a == 0) {
+            // pair 0 (or the bonus row when k = 0) kept on chip: one draw
+            // code path for either weight
+            DrawW w{p.c, -sm.R[k], 0.0f, a < k};
+            if (a < k) {
+                w.nt = -(sm.R[a] + __log2f(sm.Z[a]));
+                w.nd = -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a]));
+            }
+            hold.dlive = w.pair;
+            y = inverse_cdf_held<DT, VEC, true, NT>(trow, a < k ? stoch_row<DT>(p, s, k + 1) : trow,
+                                                    V, w, rr, &total, sm.tile_part, sm.tile_excl,
+                                                    sm.sc, hold);
+            read_again = false;
+            if (w.pair && !(total > 0.0f)) {
+                // p == q to float precision: the residual is empty; draw
+                // from p_a (read again; this almost never happens).
+                const TargetW tw{p.c, -sm.R[a]};
+                y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total,
+                                                        sm.tile_part, sm.tile_excl, sm.sc);
+            }
         }
-    } else {
-        const TargetW tw{p.c, -sm.R[k]};
-        y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total, sm.tile_part,
-                                                sm.tile_excl, sm.sc);
+    }
+    if (read_again) {
+        if (a < k) {
+            const char* drow = stoch_row<DT>(p, s, k + 1 + a);
+            const ResidualW w{p.c, -(sm.R[a] + __log2f(sm.Z[a])),
+                              -(sm.R[k + 1 + a] + __log2f(sm.Z[k + 1 + a]))};
+            y = inverse_cdf_row<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.tile_part,
+                                                   sm.tile_excl, sm.sc);
+            if (!(total > 0.0f)) {
+                // p == q to float precision: the residual is empty; draw from p_a.
+                const TargetW tw{p.c, -sm.R[a]};
+                y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total,
+                                                        sm.tile_part, sm.tile_excl, sm.sc);
+            }
+        } else {
+            const TargetW tw{p.c, -sm.R[k]};
+            y = inverse_cdf_row<DT, VEC, false, NT>(trow, nullptr, V, tw, rr, &total,
+                                                    sm.tile_part, sm.tile_excl, sm.sc);
+        }
     }
     if (tid == 0) {
         out[a] = y;
@@ -960,38 +1287,78 @@ __device__ __forceinline__ void merge_row(const float* wR, const float* wZ, int 
     for (int w = 0; w < NW; ++w) Z += wZ[r * NW + w] * fast_exp2(wR[r * NW + w] - R);
 }
 
+// Draft rounds of the held pair that a sequence-resident kernel stashes in
+// LDS beside `base` bytes of its own shared memory: a 1024-thread workgroup
+// has the CU's 160 KB to itself, two 512-thread workgroups share it.
 template <int NT>
-struct StochSeqSmem {
+constexpr int pair_stash_rounds(size_t base) {
+    const size_t budget = (NT >= 1024 ? kLdsBytesPerCu : kLdsBytesPerCu / 2) - 512;
+    const size_t per_round = (size_t)NT * 16;
+    const size_t n = base >= budget ? 0 : (budget - base) / per_round;
+    return n < (size_t)kPairHeldRounds ? (int)n : kPairHeldRounds;
+}
+
+template <int NT>
+struct StochSeqBase {
     StochFin<NT> fin;
     float wR[MAX_ROWS_STOCH * (NT / 64)];  // per-wave partial normalisers
     float wZ[MAX_ROWS_STOCH * (NT / 64)];
 };
+template <int NT, int NH>
+struct StochSeqSmem : StochSeqBase<NT> {
+    static constexpr int LR = NH > 0 ? pair_stash_rounds<NT>(sizeof(StochSeqBase<NT>)) : 0;
+    static_assert(NH == 0 || LR >= 1, "room for the draft stash");
+    uint4 stash[LR > 0 ? LR * NT : 1];
+};
 
-template <int DT, bool VEC, int NT>
+// NH: target rounds of pair 0 held in registers (0: nothing held, which
+// leaves room for more workgroups per CU).
+template <int DT, bool VEC, int NT, int NH>
 __global__ __launch_bounds__(NT) void k_stochastic_seq(Params p) {
+    using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
-    __shared__ StochSeqSmem<NT> sm;
+    __shared__ StochSeqSmem<NT, NH> sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Seq sq = seq_of(p, b);
     const int k = sq.k;
     const int rows = 2 * k + 1;
-    // Target row k first, then the pairs from position k-1 down to 0, so the
-    // rows a rejection most often lands on are the most recently read when
-    // the residual draw reads them again.
-    for (int j = 0; j < rows; ++j) {
-        const int i = k - (j + 1) / 2;
-        const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
-        const Row<DT, VEC> row(stoch_row<DT>(p, sq, r), p.V);
-        SoftAcc acc;
-        if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT, true>(row, p.c, acc);
-        else stream_softmax<DT, VEC, NT>(row, p.c, acc);
+    auto put = [&](int r, const SoftAcc& acc) {
         float R, Z;
         wave_softmax(acc, R, Z);
         if (lane == 0) {
             sm.wR[r * NW + wave] = R;
             sm.wZ[r * NW + wave] = Z;
         }
+    };
+    // Target row k first, then the pairs from position k-1 down to 0, so the
+    // pair a rejection most often lands on is read last: its target row
+    // stays in registers and the start of its draft row in LDS for the
+    // closing-token draw (the bonus row when k = 0).
+    PairHold<C, NH, NT> hold;
+    hold.stash = reinterpret_cast<C*>(sm.stash);
+    hold.lr = StochSeqSmem<NT, NH>::LR;
+    const int nlead = NH == 0 ? rows : (k > 0 ? rows - 2 : 0);
+    for (int j = 0; j < nlead; ++j) {
+        const int i = k - (j + 1) / 2;
+        const int r = (j == 0) ? k : ((j & 1) ? k + 1 + i : i);
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, r), p.V);
+        SoftAcc acc;
+        if (i < KEEP_PAIRS && j > 0) stream_softmax<DT, VEC, NT, true>(row, p.c, acc);
+        else stream_softmax<DT, VEC, NT>(row, p.c, acc);
+        put(r, acc);
+    }
+    if constexpr (NH > 0) {
+        if (k > 0) {
+            const Row<DT, VEC> row(stoch_row<DT>(p, sq, k + 1), p.V);
+            SoftAcc acc;
+            stream_softmax_stash<DT, VEC, NT, true>(row, p.c, acc, hold.stash, hold.lr);
+            put(k + 1, acc);
+        }
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, 0), p.V);
+        SoftAcc acc;
+        stream_softmax_hold<DT, VEC, NT, true, NH>(row, p.c, acc, hold.t);
+        put(0, acc);
     }
     __syncthreads();
     for (int r = tid; r < rows; r += NT) {
@@ -1005,7 +1372,12 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq(Params p) {
         sm.fin.Z[r] = Z;
     }
     __syncthreads();
-    finish_stochastic<DT, VEC, NT>(p, b, sq, sm.fin);
+    if constexpr (NH > 0) {
+        finish_stochastic<DT, VEC, NT>(p, b, sq, sm.fin, hold);
+    } else {
+        ReadAgain none;
+        finish_stochastic<DT, VEC, NT>(p, b, sq, sm.fin, none);
+    }
 }
 
 // Early-exit variant, used when no per-position diagnostics are asked for:
@@ -1014,7 +1386,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq(Params p) {
 // block-wide decision per position: after pair i every thread merges the
 // pair's per-wave partials from LDS and reaches the same verdict.
 template <int NT>
-struct StochExitSmem {
+struct StochExitBase {
     StochFin<NT> fin;
     float wR[2 * 2 * (NT / 64)];  // [pair parity][target, draft][wave]
     float wZ[2 * 2 * (NT / 64)];
@@ -1023,9 +1395,18 @@ struct StochExitSmem {
     float tv[kMaxK];  // target logit at the draft token (0 if out of range)
     float dv[kMaxK];  // draft logit at the draft token
 };
+template <int NT>
+struct StochExitSmem : StochExitBase<NT> {
+    // no stash where nothing is held (the LDS would limit the groups per CU)
+    static constexpr int LR =
+        held_rounds_exit(NT) > 0 ? pair_stash_rounds<NT>(sizeof(StochExitBase<NT>)) : 0;
+    static_assert(held_rounds_exit(NT) == 0 || LR >= 1, "room for the draft stash");
+    uint4 stash[LR > 0 ? LR * NT : 1];
+};
 
 template <int DT, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
+    using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
     __shared__ StochExitSmem<NT> sm;
     const int b = blockIdx.x;
@@ -1053,20 +1434,39 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     const int npairs = capped ? min(p.exit_pairs, k) : k;
     float* part = capped ? p.part + (size_t)b * p.rows_per_seq * p.S * 2 : nullptr;
     float Rt = 0.0f, Zt = 1.0f, Rd = 0.0f, Zd = 1.0f;
+    // The pair streamed last is the one the draw needs (the rejected pair,
+    // or the bonus row): with HOLD, each pair's draft row goes through the
+    // LDS stash and its target row through registers, overwriting the
+    // previous pair's.
+    constexpr bool HOLD = held_rounds_exit(NT) > 0;
+    PairHold<C, held_rounds_exit(NT), NT> hold;
+    hold.stash = reinterpret_cast<C*>(sm.stash);
+    hold.lr = StochExitSmem<NT>::LR;
     for (int i = 0; i < npairs; ++i) {
         float* wR = sm.wR + (i & 1) * 2 * NW;
         float* wZ = sm.wZ + (i & 1) * 2 * NW;
-        for (int half = 0; half < 2; ++half) {
-            const Row<DT, VEC> row(stoch_row<DT>(p, sq, half == 0 ? i : k + 1 + i), V);
+        // HOLD: the draft row first (into the stash), then the target row
+        // (into registers); otherwise the target row first.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool tgt = HOLD ? h == 1 : h == 0;
+            const Row<DT, VEC> row(stoch_row<DT>(p, sq, tgt ? i : k + 1 + i), V);
             SoftAcc acc;
-            stream_softmax<DT, VEC, NT>(row, c, acc);
+            if constexpr (HOLD) {
+                if (tgt)
+                    stream_softmax_hold<DT, VEC, NT, false, held_rounds_exit(NT)>(row, c, acc,
+                                                                                hold.t);
+                else stream_softmax_stash<DT, VEC, NT>(row, c, acc, hold.stash, hold.lr);
+            } else {
+                stream_softmax<DT, VEC, NT>(row, c, acc);
+            }
             float R, Z;
             wave_softmax(acc, R, Z);
             if (lane == 0) {
-                wR[half * NW + wave] = R;
-                wZ[half * NW + wave] = Z;
+                wR[(tgt ? 0 : NW) + wave] = R;
+                wZ[(tgt ? 0 : NW) + wave] = Z;
             }
-            if (i == 0 && half == 0 && gather && gx >= 0 && gx < V) {
+            if (i == 0 && h == 0 && gather && gx >= 0 && gx < V) {
                 gt = load_elem<DT>(stoch_row<DT>(p, sq, lane), gx);
                 gd = load_elem<DT>(stoch_row<DT>(p, sq, k + 1 + lane), gx);
             }
@@ -1120,38 +1520,78 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
         else if (i > a) out[i] = -1;
     }
     const float rr = p.u_sample[b];
-    float total = 0.0f;
     int y;
-    if (a < k) {
-        const ResidualW w{c, -(Rt + __log2f(Zt)), -(Rd + __log2f(Zd))};
-        y = inverse_cdf_row<DT, VEC, true, NT>(stoch_row<DT>(p, sq, a), stoch_row<DT>(p, sq, k + 1 + a),
-                                               V, w, rr, &total, sm.fin.tile_part,
-                                               sm.fin.tile_excl, sm.fin.sc);
-        if (!(total > 0.0f)) {
-            // p == q to float precision: the residual is empty; draw from p_a.
-            const TargetW tw{c, -Rt};
-            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw, rr,
+    if constexpr (HOLD) {
+        // The row (pair) the draw needs was streamed last and is held on chip:
+        // pair a after a rejection, else the bonus row k, streamed here.
+        DrawW w{c, -(Rt + __log2f(Zt)), -(Rd + __log2f(Zd)), a < k};
+        if (a == k) {
+            const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
+            SoftAcc acc;
+            stream_softmax_hold<DT, VEC, NT, false, held_rounds_exit(NT)>(row, c, acc, hold.t);
+            float R, Z;
+            wave_softmax(acc, R, Z);
+            if (lane == 0) {
+                sm.wR[(k & 1) * 2 * NW + wave] = R;
+                sm.wZ[(k & 1) * 2 * NW + wave] = Z;
+            }
+            __syncthreads();
+            float Rk, Zk;
+            merge_row<NW>(sm.wR + (k & 1) * 2 * NW, sm.wZ + (k & 1) * 2 * NW, 0, Rk, Zk);
+            (void)Zk;
+            w.nt = -Rk;
+        }
+        const char* trow = stoch_row<DT>(p, sq, a);
+        const char* drow = a < k ? stoch_row<DT>(p, sq, k + 1 + a) : trow;
+        float total = 0.0f;
+        hold.dlive = w.pair;
+        y = inverse_cdf_held<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.fin.tile_part,
+                                                sm.fin.tile_excl, sm.fin.sc, hold);
+        if (w.pair && !(total > 0.0f)) {
+            // p == q to float precision: the residual is empty; draw from p_a
+            // (read again; this almost never happens).
+            w.pair = false;
+            w.nt = -Rt;
+            ReadPair rd;
+            rd.dlive = false;
+            y = inverse_cdf_row<DT, VEC, true, NT>(trow, drow, V, w, rr, &total, sm.fin.tile_part,
+                                                   sm.fin.tile_excl, sm.fin.sc, rd);
+        }
+    } else {
+        float total = 0.0f;
+        if (a < k) {
+            const ResidualW w{c, -(Rt + __log2f(Zt)), -(Rd + __log2f(Zd))};
+            y = inverse_cdf_row<DT, VEC, true, NT>(stoch_row<DT>(p, sq, a),
+                                                   stoch_row<DT>(p, sq, k + 1 + a), V, w, rr,
+                                                   &total, sm.fin.tile_part, sm.fin.tile_excl,
+                                                   sm.fin.sc);
+            if (!(total > 0.0f)) {
+                // p == q to float precision: the residual is empty; draw from p_a.
+                const TargetW tw{c, -Rt};
+                y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, a), nullptr, V, tw,
+                                                        rr, &total, sm.fin.tile_part,
+                                                        sm.fin.tile_excl, sm.fin.sc);
+            }
+        } else {
+            // every draft token accepted: the bonus token from row k
+            const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
+            SoftAcc acc;
+            stream_softmax<DT, VEC, NT>(row, c, acc);
+            float R, Z;
+            wave_softmax(acc, R, Z);
+            if (lane == 0) {
+                sm.wR[(k & 1) * 2 * NW + wave] = R;
+                sm.wZ[(k & 1) * 2 * NW + wave] = Z;
+            }
+            __syncthreads();
+            float Rk, Zk;
+            merge_row<NW>(sm.wR + (k & 1) * 2 * NW, sm.wZ + (k & 1) * 2 * NW, 0, Rk, Zk);
+            (void)Zk;
+            const TargetW tw{c, -Rk};
+            y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, k), nullptr, V, tw, rr,
                                                     &total, sm.fin.tile_part, sm.fin.tile_excl,
                                                     sm.fin.sc);
         }
-    } else {
-        // every draft token accepted: the bonus token from row k
-        const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
-        SoftAcc acc;
-        stream_softmax<DT, VEC, NT>(row, c, acc);
-        float R, Z;
-        wave_softmax(acc, R, Z);
-        if (lane == 0) {
-            sm.wR[(k & 1) * 2 * NW + wave] = R;
-            sm.wZ[(k & 1) * 2 * NW + wave] = Z;
-        }
-        __syncthreads();
-        float Rk, Zk;
-        merge_row<NW>(sm.wR + (k & 1) * 2 * NW, sm.wZ + (k & 1) * 2 * NW, 0, Rk, Zk);
-        (void)Zk;
-        const TargetW tw{c, -Rk};
-        y = inverse_cdf_row<DT, VEC, false, NT>(stoch_row<DT>(p, sq, k), nullptr, V, tw, rr, &total,
-                                                sm.fin.tile_part, sm.fin.tile_excl, sm.fin.sc);
     }
     if (tid == 0) {
         out[a] = y;
@@ -1325,7 +1765,8 @@ __global__ __launch_bounds__(NT) void k_stochastic_finish(Params p) {
         sm.Z[r] = Z;
     }
     __syncthreads();
-    finish_stochastic<DT, VEC, NT>(p, b, sq, sm);
+    ReadAgain none;
+    finish_stochastic<DT, VEC, NT>(p, b, sq, sm, none);
 }
 
 // Continuation of a capped early exit (p.active set by k_stochastic_seq_exit,
@@ -1674,44 +2115,6 @@ __device__ int slice_draw(const Params& p, const Seq& sq, int b, int r, float u,
 constexpr int SAMPLE_ROUNDS = kSampleSeqRounds;
 constexpr int SAMPLE_UNROLL = 4;  // rounds loaded per step (SAMPLE_ROUNDS a multiple)
 
-// A thread's chunk of every round of a row, kept in registers: one member
-// per round (no array, which a run-time pick would turn into a scratch
-// buffer), set and picked through compile-time indices.
-template <typename C, int N>
-struct HeldRounds : HeldRounds<C, N - 1> {
-    static constexpr bool kHeld = true;
-    C last;
-    template <int J>
-    __device__ __forceinline__ C& at() {
-        if constexpr (J == N - 1) return last;
-        else return HeldRounds<C, N - 1>::template at<J>();
-    }
-    template <typename C2>
-    __device__ __forceinline__ C2 round(int rd) const {  // rd uniform over the block
-        if (rd == N - 1) return last;
-        return HeldRounds<C, N - 1>::template round<C2>(rd);
-    }
-};
-template <typename C>
-struct HeldRounds<C, 1> {
-    static constexpr bool kHeld = true;
-    C last;
-    template <int J>
-    __device__ __forceinline__ C& at() { return last; }
-    template <typename C2>
-    __device__ __forceinline__ C2 round(int) const { return last; }
-};
-
-// held.at<J>() = buf[J - base] for the rounds J in [base, base + U) (base is
-// a compile-time constant once the caller's loop is unrolled).
-template <int J, int U, typename H, typename C>
-__device__ __forceinline__ void store_held(H& held, int base, const C* buf) {
-    if constexpr (J < kSampleHeldRounds) {
-        if (J >= base && J < base + U) held.template at<J>() = buf[J - base];
-        store_held<J + 1, U>(held, base, buf);
-    }
-}
-
 // HOLD (rows of at most kSampleHeldRounds rounds): every thread also keeps
 // the chunks it streamed, so the round holding the draw is scanned from
 // registers instead of being read again.
@@ -1766,7 +2169,7 @@ __global__ __launch_bounds__(NT) void k_sample_seq(Params p) {
                 rs[q * SAMPLE_UNROLL + u] = su;
                 acc.s0 += su;
             }
-            if constexpr (HOLD) store_held<0, SAMPLE_UNROLL>(held, q * SAMPLE_UNROLL, buf);
+            if constexpr (HOLD) store_held<0, RMAX, SAMPLE_UNROLL>(held, q * SAMPLE_UNROLL, buf);
         } else {
 #pragma unroll
             for (int u = 0; u < SAMPLE_UNROLL; ++u) rs[q * SAMPLE_UNROLL + u] = 0.0f;
@@ -2036,12 +2439,17 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         if (e) return e;
         return launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
     }
-    if (seq && p.B >= kSeqWideMinB)
-        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
-                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE,
-                               stream);
+    if (seq && p.B >= kSeqWideMinB) {
+        if (!p.dbg)
+            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
+        constexpr int NH = held_rounds_seq(NT_SEQ_WIDE);
+        return p.B <= kSeqWideHoldMaxB
+                   ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, NH>, p, p.B, NT_SEQ_WIDE, stream)
+                   : launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, 0>, p, p.B, NT_SEQ_WIDE, stream);
+    }
     if (seq)
-        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream)
+        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ, held_rounds_seq(NT_SEQ)>, p, p.B,
+                               NT_SEQ, stream)
                      : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
     int e = launch_row_stats<DT, VEC, true>(p, stream);
     if (e) return e;

@@ -110,7 +110,7 @@ def make_stochastic(seed, B, k, V, dtype, tau, special=None):
         d64[rng.random(d64.shape) < 0.1] = -np.inf
         t64[..., 0] = 0.0  # keep a finite entry in every row
         d64[..., 0] = 0.0
-    if special == "equal":
+    if special in ("equal", "equaloov"):
         d64 = t64[:, :k].copy()
     if special == "onehot":
         d64 = np.full((B, k, V), -np.inf)
@@ -122,7 +122,9 @@ def make_stochastic(seed, B, k, V, dtype, tau, special=None):
                            dtype)
     else:
         x = W.gumbel_max(rng, W.as_f64(d, dtype), tau)
-    if special == "oov":
+    if special in ("oov", "equaloov"):
+        # out of range: p = q = 0, a rejection (with "equaloov" the residual
+        # of equal rows is then empty and the draw falls back to p)
         x[::2, 0] = -1
         x[1::2, -1] = V + 5
     ua = W.exact_uniforms(rng, B * k).reshape(B, k)
@@ -167,6 +169,19 @@ STOCH_CASES = [
     (7, 3, 2053, W.F32, 0.02, 0, True, "neginf"),
     # a vocabulary past a million entries
     (2, 1, 1048583, W.BF16, 1.0, 0, False, None),
+    # the pair streamed last kept on chip for the draw: rows longer than the
+    # rounds held in registers (fp32 at 1024 threads, bf16 at 512), both
+    # sides of the 512 sequences up to which 512-thread groups hold, element
+    # rows, and the empty-residual fallback after a held draw (full read,
+    # plain and capped early exits)
+    (200, 3, 50000, W.F32, 1.0, 0, False, None),
+    (300, 2, 70001, W.BF16, 1.0, 0, False, None),
+    (512, 2, 3001, W.BF16, 1.0, 0, False, None),
+    (520, 2, 3001, W.BF16, 1.0, 0, False, None),
+    (256, 3, 4103, W.BF16, 1.0, 0, False, "equaloov"),
+    (256, 8, 2053, W.F32, 1.0, 0, False, "equaloov"),
+    (400, 3, 2053, W.BF16, 1.0, 0, True, "equaloov"),
+    (256, 6, 128256, W.BF16, 1.0, 0, False, "close"),
 ]
 
 
@@ -181,8 +196,10 @@ def test_stochastic_small(case):
     assert rep.ok(), rep.summary()
     if special == "equal":
         assert np.all(a == k)
-    if special == "oov":
+    if special in ("oov", "equaloov"):
         assert np.all(a[::2] == 0)
+    if special == "equaloov":
+        assert np.all(a[1::2] == k - 1)
 
 
 def make_greedy(seed, B, G, k, V, dtype, ties=False):
