@@ -169,36 +169,81 @@ struct Row<DT, false> {
 };
 
 // ------------------------------------------------------------------------
-// Wave64 and block reductions.
+// Wave64 and block reductions.  The wave-level steps move data between
+// lanes with DPP (row shifts, mirrors and row broadcasts, GFX9-family
+// controls): plain VALU operations, where a shuffle (ds_bpermute) takes an
+// LDS round trip per step.  Reductions end in lane 63 and are broadcast
+// from it, so every lane gets the same value.
+constexpr int DPP_QUAD_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHR1 = 0x111;       // row_shr:n = 0x110 + n
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_BCAST15 = 0x142;    // lane 15 of a row to the next row
+constexpr int DPP_ROW_BCAST31 = 0x143;    // lane 31 to rows 2 and 3
+constexpr int DPP_WAVE_SHR1 = 0x138;      // the whole wave shifted by one lane
+
+// src from the lane CTRL names; lanes outside ROWM, or whose source lane
+// does not exist, get `old`.
+template <int CTRL, int ROWM = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int src) {
+    return __builtin_amdgcn_update_dpp(old, src, CTRL, ROWM, 0xF, false);
+}
+template <int CTRL, int ROWM = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float src) {
+    return __int_as_float(dpp_i<CTRL, ROWM>(__float_as_int(old), __float_as_int(src)));
+}
+__device__ __forceinline__ float lane63_f(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Reduction over the wave with op (sum, max, min): within quads, then
+// 8- and 16-lane rows, then the rows into lane 63.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+    if constexpr (sizeof(T) == 4 && T(0.5) != T(0)) {  // float
+        v = op(v, dpp_f<DPP_QUAD_XOR1>(v, v));
+        v = op(v, dpp_f<DPP_QUAD_XOR2>(v, v));
+        v = op(v, dpp_f<DPP_ROW_HALF_MIRROR>(v, v));
+        v = op(v, dpp_f<DPP_ROW_MIRROR>(v, v));
+        v = op(v, dpp_f<DPP_ROW_BCAST15, 0xA>(v, v));
+        v = op(v, dpp_f<DPP_ROW_BCAST31, 0xC>(v, v));
+        return lane63_f(v);
+    } else {
+        v = op(v, dpp_i<DPP_QUAD_XOR1>(v, v));
+        v = op(v, dpp_i<DPP_QUAD_XOR2>(v, v));
+        v = op(v, dpp_i<DPP_ROW_HALF_MIRROR>(v, v));
+        v = op(v, dpp_i<DPP_ROW_MIRROR>(v, v));
+        v = op(v, dpp_i<DPP_ROW_BCAST15, 0xA>(v, v));
+        v = op(v, dpp_i<DPP_ROW_BCAST31, 0xC>(v, v));
+        return __builtin_amdgcn_readlane(v, 63);
+    }
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](int a, int b) { return min(a, b); });
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce(v, [](int a, int b) { return max(a, b); });
 }
+// Inclusive prefix sum over the wave: shifts by 1, 2, 4, 8 within each row
+// of 16 lanes, then each row adds the totals of the rows before it.
 __device__ __forceinline__ float wave_incl_scan(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const float n = __shfl_up(v, o);
-        if (lane >= o) v += n;
-    }
+    v += dpp_f<DPP_ROW_SHR1>(0.0f, v);
+    v += dpp_f<DPP_ROW_SHR1 + 1>(0.0f, v);
+    v += dpp_f<DPP_ROW_SHR1 + 3>(0.0f, v);
+    v += dpp_f<DPP_ROW_SHR1 + 7>(0.0f, v);
+    v += dpp_f<DPP_ROW_BCAST15, 0xA>(0.0f, v);
+    v += dpp_f<DPP_ROW_BCAST31, 0xC>(0.0f, v);
     return v;
 }
+// The value of the lane below (0 in lane 0).
+__device__ __forceinline__ float wave_shift_up1(float v) { return dpp_f<DPP_WAVE_SHR1>(0.0f, v); }
 // Larger value wins; equal values go to the lower index.
 __device__ __forceinline__ bool argmax_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);
@@ -230,8 +275,7 @@ __device__ __forceinline__ float block_excl_scan(float v, float* total, Scratch<
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float incl = wave_incl_scan(v);
-    float excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0f;
+    const float excl = wave_shift_up1(incl);
     if (lane == 63) sc.f[wave] = incl;
     __syncthreads();
     float off = 0.0f, tot = 0.0f;
