@@ -135,7 +135,11 @@ def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -
             if spec.k >= 6 and spec.B <= 1024:  # capped pass, then the spread continuation
                 return "k_stochastic_seq_exit (capped) + k_exit_stats + k_draw_tiles"
             return "k_stochastic_seq_exit"
-        return "k_stochastic_seq" if uniform else "k_row_stats"
+        if not uniform:
+            return "k_row_stats"
+        # up to 256 sequences (one 1024-thread group each) the full read runs
+        # in position order in the early-exit kernel's full-read variant
+        return "k_stochastic_seq_exit (full read)" if spec.B <= 256 else "k_stochastic_seq"
     return "k_row_stats"
 
 

@@ -93,21 +93,28 @@ constexpr int kSampleSeqRounds = 32;
 // Rows of at most kSampleHeldRounds rounds also keep every chunk they stream
 // in registers, so the draw scans its round without reading it again.
 constexpr int kSampleHeldRounds = 16;
-// The sequence-resident stochastic kernels keep the row pair they stream
-// last on chip for the closing-token draw, which would otherwise read both
-// rows again: each thread's chunks of the first rounds of the target row in
-// registers (4 VGPRs per round for 16-byte chunks), and as many rounds of
-// the draft row as fit in the LDS left beside the kernel's own
-// (kLdsBytesPerCu per CU).  Rounds held, per kernel and workgroup size: as
-// many as fit in the 128 VGPRs that four waves per SIMD allow without
-// spilling, except where holding measured no gain (the early exit with
-// 512-thread groups, two or more per CU: 136.8 against 137.5 us on B=512,
-// k=3, V=129280 bf16).  Measured per call, V=128256 bf16: full read B=256,
-// k=8 186.7 -> 186.4 us, B=512 k=3 (V=129280) 171.6 -> 170.5 us, B=1024 k=3
-// 340.5 -> 335.5 us; capped early exit B=256 k=8 108.8 -> 104.5 us.
-#ifndef SV_HOLD_SEQ_1024
-#define SV_HOLD_SEQ_1024 12
-#endif
+// The sequence-resident stochastic kernels keep the row pair they have just
+// streamed on chip for the closing-token draw, which would otherwise read
+// both rows again: each thread's chunks of the first rounds of the target
+// row in registers (4 VGPRs per round for 16-byte chunks), and as many
+// rounds of the draft row as fit in the LDS left beside the kernel's own
+// (kLdsBytesPerCu per CU).  Rounds held: as many as fit in the 128 VGPRs
+// that four waves per SIMD allow without spilling, except where holding
+// measured no gain (the early exit with 512-thread groups, two or more per
+// CU: 136.8 against 137.5 us on B=512, k=3, V=129280 bf16).
+//
+// With 1024-thread groups (up to 256 sequences) the early exit and the full
+// read are one kernel that streams the pairs in position order, holding
+// each, and draws right after the first rejection, so whichever pair a
+// sequence rejects at is on chip; the full read then streams the rest of
+// the rows for the diagnostics.  Per call, B=256, k=8, V=128256 bf16, full
+// read, against streaming pair 0 last and holding only it: the peaked batch
+// (mean accepted length 1.2) 185.4 -> 178.2 us; half the sequences
+// accepting every draft (mean 4.0) 185.3 -> 177.4, a quarter (mean 2.0)
+// 185.3 -> 179.5; but drafts rejected almost always at position 0 (mean
+// 0.1) 185.9 -> 189.3, and every draft accepted 179.8 -> 184.8 (a barrier
+// per pair).  With 512-thread groups the previous order stays (position
+// order measured up to 12 us slower on short rows: B=300, k=8, V=32000).
 #ifndef SV_HOLD_SEQ_512
 #define SV_HOLD_SEQ_512 16
 #endif
@@ -124,7 +131,7 @@ constexpr int kPairHeldRounds = 16;  // the most any kernel holds
 // nothing is held there (B=700, k=8, V=32000 bf16: 132.6 us without, 161.1
 // with; B=1024, k=3, V=128256: 339.4 without, 334.5 with, two full rounds).
 constexpr int kSeqWideHoldMaxB = 512;
-constexpr int held_rounds_seq(int nt) { return nt >= 1024 ? SV_HOLD_SEQ_1024 : SV_HOLD_SEQ_512; }
+constexpr int kSeqWideHeldRounds = SV_HOLD_SEQ_512;  // full read, 512-thread groups
 constexpr int held_rounds_exit(int nt) { return nt >= 1024 ? SV_HOLD_EXIT_1024 : SV_HOLD_EXIT_512; }
 constexpr size_t kLdsBytesPerCu = 160 * 1024;
 constexpr long long kSampleSeqBaseElems = 40960;

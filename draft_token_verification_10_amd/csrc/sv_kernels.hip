@@ -1439,20 +1439,24 @@ struct StochExitBase {
     float tv[kMaxK];  // target logit at the draft token (0 if out of range)
     float dv[kMaxK];  // draft logit at the draft token
 };
-template <int NT>
+template <int NT, int NH>
 struct StochExitSmem : StochExitBase<NT> {
     // no stash where nothing is held (the LDS would limit the groups per CU)
-    static constexpr int LR =
-        held_rounds_exit(NT) > 0 ? pair_stash_rounds<NT>(sizeof(StochExitBase<NT>)) : 0;
-    static_assert(held_rounds_exit(NT) == 0 || LR >= 1, "room for the draft stash");
+    static constexpr int LR = NH > 0 ? pair_stash_rounds<NT>(sizeof(StochExitBase<NT>)) : 0;
+    static_assert(NH == 0 || LR >= 1, "room for the draft stash");
     uint4 stash[LR > 0 ? LR * NT : 1];
 };
 
-template <int DT, bool VEC, int NT>
+// NH: target rounds of the pair being streamed held in registers (0: none).
+// FULL: the full read (diagnostics asked for): p and q at every position go
+// to p.dbg, and once the token is drawn the rest of the rows are streamed
+// too, so every row is read once and the draw still finds the pair it needs
+// on chip.
+template <int DT, bool VEC, int NT, int NH, bool FULL>
 __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     using C = Chunk<DT, VEC>;
     constexpr int NW = NT / 64;
-    __shared__ StochExitSmem<NT> sm;
+    __shared__ StochExitSmem<NT, NH> sm;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Seq sq = seq_of(p, b);
@@ -1482,10 +1486,11 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     // or the bonus row): with HOLD, each pair's draft row goes through the
     // LDS stash and its target row through registers, overwriting the
     // previous pair's.
-    constexpr bool HOLD = held_rounds_exit(NT) > 0;
-    PairHold<C, held_rounds_exit(NT), NT> hold;
+    constexpr bool HOLD = NH > 0;
+    constexpr bool full = FULL;  // never capped
+    PairHold<C, NH, NT> hold;
     hold.stash = reinterpret_cast<C*>(sm.stash);
-    hold.lr = StochExitSmem<NT>::LR;
+    hold.lr = StochExitSmem<NT, NH>::LR;
     for (int i = 0; i < npairs; ++i) {
         float* wR = sm.wR + (i & 1) * 2 * NW;
         float* wZ = sm.wZ + (i & 1) * 2 * NW;
@@ -1497,9 +1502,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             const Row<DT, VEC> row(stoch_row<DT>(p, sq, tgt ? i : k + 1 + i), V);
             SoftAcc acc;
             if constexpr (HOLD) {
-                if (tgt)
-                    stream_softmax_hold<DT, VEC, NT, false, held_rounds_exit(NT)>(row, c, acc,
-                                                                                hold.t);
+                if (tgt) stream_softmax_hold<DT, VEC, NT, false, NH>(row, c, acc, hold.t);
                 else stream_softmax_stash<DT, VEC, NT>(row, c, acc, hold.stash, hold.lr);
             } else {
                 stream_softmax<DT, VEC, NT>(row, c, acc);
@@ -1544,6 +1547,10 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             pi = fast_exp2(fmaf(sm.tv[i], c, -Rt)) / Zt;
             qi = fast_exp2(fmaf(sm.dv[i], c, -Rd)) / Zd;
         }
+        if (full && tid == 0) {
+            p.dbg[(sq.d0 + i) * 2] = pi;
+            p.dbg[(sq.d0 + i) * 2 + 1] = qi;
+        }
         if (!(sm.uv[i] * qi < pi)) {  // the same verdict in every thread
             a = i;
             break;
@@ -1572,7 +1579,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
         if (a == k) {
             const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
             SoftAcc acc;
-            stream_softmax_hold<DT, VEC, NT, false, held_rounds_exit(NT)>(row, c, acc, hold.t);
+            stream_softmax_hold<DT, VEC, NT, false, NH>(row, c, acc, hold.t);
             float R, Z;
             wave_softmax(acc, R, Z);
             if (lane == 0) {
@@ -1640,6 +1647,50 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
     if (tid == 0) {
         out[a] = y;
         if (p.accept_len) p.accept_len[b] = a;
+    }
+    if (full && a < k) {
+        // The rows after the rejection, for the diagnostics: p and q at the
+        // later positions (one barrier per pair, which measured faster than
+        // streaming them all before one merge), then the bonus row, read
+        // like every other row.
+        for (int i = a + 1; i < k; ++i) {
+            float* wR = sm.wR + (i & 1) * 2 * NW;
+            float* wZ = sm.wZ + (i & 1) * 2 * NW;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const Row<DT, VEC> row(stoch_row<DT>(p, sq, h == 0 ? i : k + 1 + i), V);
+                SoftAcc acc;
+                stream_softmax<DT, VEC, NT>(row, c, acc);
+                float R, Z;
+                wave_softmax(acc, R, Z);
+                if (lane == 0) {
+                    wR[h * NW + wave] = R;
+                    wZ[h * NW + wave] = Z;
+                }
+            }
+            __syncthreads();
+            merge_row<NW>(wR, wZ, 0, Rt, Zt);
+            merge_row<NW>(wR, wZ, 1, Rd, Zd);
+            if (tid == 0) {
+                const int xi = sm.xv[i];
+                float pi = 0.0f, qi = 0.0f;
+                if (xi >= 0 && xi < V) {
+                    pi = fast_exp2(fmaf(sm.tv[i], c, -Rt)) / Zt;
+                    qi = fast_exp2(fmaf(sm.dv[i], c, -Rd)) / Zd;
+                }
+                p.dbg[(sq.d0 + i) * 2] = pi;
+                p.dbg[(sq.d0 + i) * 2 + 1] = qi;
+            }
+        }
+        const Row<DT, VEC> row(stoch_row<DT>(p, sq, k), V);
+        SoftAcc acc;
+        stream_softmax<DT, VEC, NT>(row, c, acc);
+        float R, Z;
+        wave_softmax(acc, R, Z);
+        if (lane == 0) {
+            sm.wR[(k & 1) * 2 * NW + wave] = R;
+            sm.wZ[(k & 1) * 2 * NW + wave] = Z;
+        }
     }
 }
 
@@ -2474,10 +2525,13 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         return hold ? launch1(k_sample_seq<DT, VEC, NT_SEQ, true>, p, p.B, NT_SEQ, stream)
                     : launch1(k_sample_seq<DT, VEC, NT_SEQ, false>, p, p.B, NT_SEQ, stream);
     }
+    constexpr int NHX = held_rounds_exit(NT_SEQ), NHXW = held_rounds_exit(NT_SEQ_WIDE);
     if (seq && p.active) {  // capped early exit, then the spread continuation
         const bool wide = p.B >= kSeqWideMinB;
-        int e = wide ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream)
-                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
+        int e = wide ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHXW, false>, p, p.B,
+                               NT_SEQ_WIDE, stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ, NHX, false>, p, p.B, NT_SEQ,
+                               stream);
         if (e) return e;
         e = launch1(k_exit_stats<DT, VEC>, p, kExitStatsGrid, NT_ROW, stream);
         if (e) return e;
@@ -2485,16 +2539,20 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
     }
     if (seq && p.B >= kSeqWideMinB) {
         if (!p.dbg)
-            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE>, p, p.B, NT_SEQ_WIDE, stream);
-        constexpr int NH = held_rounds_seq(NT_SEQ_WIDE);
-        return p.B <= kSeqWideHoldMaxB
-                   ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, NH>, p, p.B, NT_SEQ_WIDE, stream)
-                   : launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, 0>, p, p.B, NT_SEQ_WIDE, stream);
+            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHXW, false>, p, p.B,
+                           NT_SEQ_WIDE, stream);
+        if (p.B > kSeqWideHoldMaxB)
+            return launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, 0>, p, p.B, NT_SEQ_WIDE, stream);
+        constexpr int NH = kSeqWideHeldRounds;
+        return launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, NH>, p, p.B, NT_SEQ_WIDE, stream);
     }
+    // one group per sequence, up to 256: the early exit, and the full read
+    // in position order (the same kernel, with p.dbg)
     if (seq)
-        return p.dbg ? launch1(k_stochastic_seq<DT, VEC, NT_SEQ, held_rounds_seq(NT_SEQ)>, p, p.B,
-                               NT_SEQ, stream)
-                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ>, p, p.B, NT_SEQ, stream);
+        return p.dbg ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ, NHX, true>, p, p.B, NT_SEQ,
+                               stream)
+                     : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ, NHX, false>, p, p.B, NT_SEQ,
+                               stream);
     int e = launch_row_stats<DT, VEC, true>(p, stream);
     if (e) return e;
     if (p.slice_draw) return launch1(k_sample_draw<DT, VEC>, p, p.B, NT_SAMPLE, stream);

@@ -76,7 +76,8 @@ def test_commit_bytes():
 
 def test_kernel_names_follow_layouts():
     s2, s1 = W.SPECS[2], W.SPECS[1]
-    assert bench.kernel_name(s2, "stochastic") == "k_stochastic_seq"
+    assert bench.kernel_name(s2, "stochastic") == "k_stochastic_seq_exit (full read)"
+    assert bench.kernel_name(W.SPECS[3], "stochastic") == "k_stochastic_seq"
     # without diagnostics: the capped early exit for k >= 6 (B=256, k=8), the
     # plain one below (B=512, k=3)
     assert bench.kernel_name(s2, "stochastic", diagnostics=False).startswith(
@@ -84,7 +85,7 @@ def test_kernel_names_follow_layouts():
     assert bench.kernel_name(W.SPECS[3], "stochastic", diagnostics=False) == "k_stochastic_seq_exit"
     assert bench.kernel_name(s2, "greedy") == "k_greedy_seq"
     assert bench.kernel_name(s2, "ragged", uniform=False) == "k_row_stats"
-    assert bench.kernel_name(s2, "ragged", uniform=True) == "k_stochastic_seq"
+    assert bench.kernel_name(s2, "ragged", uniform=True) == "k_stochastic_seq_exit (full read)"
     assert bench.kernel_name(s2, "sample") == "k_sample_seq"
     assert bench.kernel_name(s1, "sample") == "k_row_stats"
     assert bench.sample_one_pass(512, 98304, 2) and not bench.sample_one_pass(512, 128256, 2)
