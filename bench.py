@@ -45,7 +45,7 @@ figures); "warm" repeats the timing on one copy.
 Other switches, for the profiler:
   --copy-calibration   time a plain device-to-device copy of 1 GiB (the
                        reference kernel for HBM byte counters)
-  --record-traffic KEY --fetch-csv F --write-csv W --kernels K1,K2 [--source S]
+  --record-traffic KEY --fetch-csv F --write-csv W --kernels 'K1;K2' [--source S]
                        (no GPU) store one call's HBM bytes from a FETCH_SIZE
                        and a WRITE_SIZE rocprofv3 run in profiles/traffic.json
   --no-cpu-baseline    skip the CPU oracle timing
@@ -565,7 +565,8 @@ def main():
     ap.add_argument("--fetch-csv", default=None)
     ap.add_argument("--write-csv", default=None)
     ap.add_argument("--kernels", default=None,
-                    help="comma-separated kernel names of one call, as in the CSVs")
+                    help="kernel names of one call, as in the CSVs, separated by ';' "
+                         "(template arguments hold commas)")
     ap.add_argument("--source", default="", help="the profile summary quoting the counts")
     args = ap.parse_args()
 
@@ -573,7 +574,7 @@ def main():
         if not (args.fetch_csv and args.write_csv and args.kernels):
             ap.error("--record-traffic needs --fetch-csv, --write-csv and --kernels")
         e = record_traffic(args.record_traffic, args.fetch_csv, args.write_csv,
-                           args.kernels.split(","), args.source)
+                           args.kernels.split(";"), args.source)
         print(json.dumps({args.record_traffic: e}))
         return
 
