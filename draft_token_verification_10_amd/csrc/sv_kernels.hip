@@ -269,8 +269,15 @@ struct Scratch {
     int j[NW];
 };
 
-// Block-wide exclusive prefix sum; *total gets the block sum.  All threads call.
-template <int NT>
+// Block-wide operations.  All threads call.  Each publishes per-wave values
+// in its own array of sc (f, i or j) behind a barrier; TRAIL adds a second
+// barrier after the reads, so that the same array can be written again
+// right away.  Without it the caller must order the next write of that
+// array after a barrier of its own (as a different operation's first
+// barrier does).
+//
+// Exclusive prefix sum; *total gets the block sum.
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ float block_excl_scan(float v, float* total, Scratch<NT>& sc) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -284,12 +291,12 @@ __device__ __forceinline__ float block_excl_scan(float v, float* total, Scratch<
         if (w < wave) off += sc.f[w];
         tot += sc.f[w];
     }
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     *total = tot;
     return off + excl;
 }
 
-template <int NT>
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ int block_min_i(int v, Scratch<NT>& sc) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -299,11 +306,11 @@ __device__ __forceinline__ int block_min_i(int v, Scratch<NT>& sc) {
     int r = sc.i[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) r = min(r, sc.i[w]);
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     return r;
 }
 
-template <int NT>
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ int block_max_i(int v, Scratch<NT>& sc) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -313,7 +320,7 @@ __device__ __forceinline__ int block_max_i(int v, Scratch<NT>& sc) {
     int r = sc.j[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) r = max(r, sc.j[w]);
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     return r;
 }
 
@@ -899,7 +906,7 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
         run += s;
     }
     float total;
-    const float excl = block_excl_scan<NT>(run, &total, sc);
+    const float excl = block_excl_scan<NT, false>(run, &total, sc);
     const float T = r * total;
     int cross = INT_MAX;
     {
@@ -917,7 +924,7 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
             }
         }
     }
-    cross = block_min_i<NT>(cross, sc);  // its barrier also publishes tile_excl
+    cross = block_min_i<NT, false>(cross, sc);  // its barrier also publishes tile_excl
     *total_out = total;
     if (cross == INT_MAX) {
         // No cumulative sum exceeds r * total (r = 1, or rounding left r *
@@ -931,8 +938,11 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
             const int t = tid * tpt + j;
             if (t < g.nt_all && mine[j] > 0.0f) lt = t;
         }
-        cross = block_max_i<NT>(lt, sc);
-        if (cross < 0) return 0;  // no positive weight anywhere
+        cross = block_max_i<NT, false>(lt, sc);
+        if (cross < 0) {  // no positive weight anywhere
+            __syncthreads();
+            return 0;
+        }
     }
 
     // Pass B: scan inside the crossing tile.
@@ -948,9 +958,9 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
             if (w > 0.0f) tile_last = nch * E + tid;
         }
         float tot;
-        const float ex = block_excl_scan<NT>(w, &tot, sc);
+        const float ex = block_excl_scan<NT, false>(w, &tot, sc);
         if (w > 0.0f && cum + (ex + w) > T) found = nch * E + tid;
-        found = block_min_i<NT>(found, sc);
+        found = block_min_i<NT, false>(found, sc);
     } else {
         for (int rd = cross * g.m; rd < min(g.rounds, (cross + 1) * g.m); ++rd) {
             const int ci = rd * NT + tid;
@@ -971,7 +981,7 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
                 for (int e = 0; e < E; ++e) wv[e] = 0.0f;
             }
             float tot;
-            const float ex = block_excl_scan<NT>(loc, &tot, sc);
+            const float ex = block_excl_scan<NT, false>(loc, &tot, sc);
             int f = INT_MAX;
             float run_e = ex;
 #pragma unroll
@@ -979,12 +989,15 @@ __device__ __forceinline__ int cdf_select(const Row<DT, VEC>& tr, const Row<DT, 
                 run_e += wv[e];
                 if (f == INT_MAX && wv[e] > 0.0f && cum + run_e > T) f = ci * E + e;
             }
-            found = block_min_i<NT>(f, sc);
+            found = block_min_i<NT, false>(f, sc);
             if (found != INT_MAX) break;  // uniform
             cum += tot;
         }
     }
-    if (found != INT_MAX) return found;
+    if (found != INT_MAX) {
+        __syncthreads();  // the one trailing barrier (see the block operations)
+        return found;
+    }
     return max(block_max_i<NT>(tile_last, sc), 0);
 }
 
