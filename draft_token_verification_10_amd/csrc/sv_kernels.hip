@@ -60,6 +60,16 @@ constexpr int LOAD_POLICY_NT = 2;
 // (measured: a small gain at B=512, none at B=256, where the re-read comes
 // from HBM whichever pair it is).
 constexpr int KEEP_PAIRS = 1;
+// The position-order kernel reads the pairs of positions below this with
+// ordinary loads: if such a pair is rejected, what is not held on chip is
+// read again right away and part of it is then still cached, while long
+// accepted runs keep the non-temporal stream.  Measured per call (B=256,
+// k=8, V=128256 bf16; 0 / 1 / 2 / 3 / every position): capped early exit
+// 104.9 / 104.2 / 100.8 / 101.1 / 101.4 us; full read 175.1 / 173.9 / 174.5
+// / 174.7 / 172.8; full read with every draft accepted 182.8 / 182.6 /
+// 181.6 / 186.1 / 197.5; B=512, k=3, V=129280 plain early exit 134.0 /
+// 128.9 / 130.7 / 131.1 / 131.0.
+constexpr int EXIT_KEEP_PAIRS = 2;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -1514,11 +1524,20 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             const bool tgt = HOLD ? h == 1 : h == 0;
             const Row<DT, VEC> row(stoch_row<DT>(p, sq, tgt ? i : k + 1 + i), V);
             SoftAcc acc;
-            if constexpr (HOLD) {
-                if (tgt) stream_softmax_hold<DT, VEC, NT, false, NH>(row, c, acc, hold.t);
-                else stream_softmax_stash<DT, VEC, NT>(row, c, acc, hold.stash, hold.lr);
+            if (i < EXIT_KEEP_PAIRS) {  // uniform
+                if constexpr (HOLD) {
+                    if (tgt) stream_softmax_hold<DT, VEC, NT, true, NH>(row, c, acc, hold.t);
+                    else stream_softmax_stash<DT, VEC, NT, true>(row, c, acc, hold.stash, hold.lr);
+                } else {
+                    stream_softmax<DT, VEC, NT, true>(row, c, acc);
+                }
             } else {
-                stream_softmax<DT, VEC, NT>(row, c, acc);
+                if constexpr (HOLD) {
+                    if (tgt) stream_softmax_hold<DT, VEC, NT, false, NH>(row, c, acc, hold.t);
+                    else stream_softmax_stash<DT, VEC, NT>(row, c, acc, hold.stash, hold.lr);
+                } else {
+                    stream_softmax<DT, VEC, NT>(row, c, acc);
+                }
             }
             float R, Z;
             wave_softmax(acc, R, Z);
