@@ -182,6 +182,11 @@ STOCH_CASES = [
     (256, 8, 2053, W.F32, 1.0, 0, False, "equaloov"),
     (400, 3, 2053, W.BF16, 1.0, 0, True, "equaloov"),
     (256, 6, 128256, W.BF16, 1.0, 0, False, "close"),
+    # the full read in position order (up to 256 sequences) when every
+    # draft is accepted (the bonus row held) and with high acceptance on
+    # element rows
+    (256, 5, 4103, W.BF16, 1.0, 0, False, "equal"),
+    (224, 6, 50000, W.F32, 0.8, 0, True, "close"),
 ]
 
 
