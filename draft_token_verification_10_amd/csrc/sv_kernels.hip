@@ -1378,6 +1378,8 @@ struct StochSeqSmem : StochSeqBase<NT> {
     uint4 stash[LR > 0 ? LR * NT : 1];
 };
 
+// The full read with 512-thread groups (more sequences than CUs; up to 256
+// sequences the full read runs in position order in k_stochastic_seq_exit).
 // NH: target rounds of pair 0 held in registers (0: nothing held, which
 // leaves room for more workgroups per CU).
 template <int DT, bool VEC, int NT, int NH>
@@ -1447,11 +1449,13 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq(Params p) {
     }
 }
 
-// Early-exit variant, used when no per-position diagnostics are asked for:
-// rows stream in position order and a sequence stops reading at its first
-// rejection, because no later row can change accept_len or tokens.  One
-// block-wide decision per position: after pair i every thread merges the
-// pair's per-wave partials from LDS and reaches the same verdict.
+// Position-order kernel.  Without per-position diagnostics (the early
+// exit) a sequence stops reading at its first rejection, because no later
+// row can change accept_len or tokens; its full-read variant (FULL, up to
+// 256 sequences) draws there too and then reads the remaining rows for the
+// diagnostics.  One block-wide decision per position: after pair i every
+// thread merges the pair's per-wave partials from LDS and reaches the same
+// verdict.
 template <int NT>
 struct StochExitBase {
     StochFin<NT> fin;
