@@ -699,10 +699,9 @@ def main():
     ms, wall = time_calls(fns, args.steps, args.warmup, torch)
     result = line(spec, mode, ms, nbytes, kern, traffic_key, args, wall, extra_cfg)
     result["per_call_us"] = per_call_us(fns, min(args.steps, 100), torch)
-    if ms < 0.05:
-        # launch-bound: the device time of a call without the binding's host
-        # overhead (20 calls captured in a graph, 10 replays)
-        result["graph_us_per_call"] = round(graph_us(fns, 20, 10, torch), 2)
+    # the device time of a call without the binding's host overhead (20
+    # calls captured in a graph, 10 replays), beside the eager mean
+    result["graph_us_per_call"] = round(graph_us(fns, 20, 10, torch), 2)
     if nc > 1:
         ms_w, _ = time_calls(fns[:1], args.steps, args.warmup, torch)
         result["warm"] = {"ms_per_step": round(ms_w, 5),
