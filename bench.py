@@ -137,9 +137,15 @@ def kernel_name(spec, mode: str, diagnostics=True, greedy=False, uniform=True) -
             return "k_stochastic_seq_exit"
         if not uniform:
             return "k_row_stats"
-        # up to 256 sequences (one 1024-thread group each) the full read runs
-        # in position order in the early-exit kernel's full-read variant
-        return "k_stochastic_seq_exit (full read)" if spec.B <= 256 else "k_stochastic_seq"
+        # the full read runs in position order in the early-exit kernel's
+        # full-read variant up to 256 sequences (one 1024-thread group each),
+        # and from 384 to 512 sequences with rows of at least 160000 bytes
+        # (512-thread groups, two per CU)
+        from draft_token_verification_10_amd.workloads import BF16
+        row_bytes = spec.V * (2 if spec.dtype == BF16 else 4)
+        if spec.B <= 256 or (384 <= spec.B <= 512 and row_bytes >= 160000):
+            return "k_stochastic_seq_exit (full read)"
+        return "k_stochastic_seq"
     return "k_row_stats"
 
 

@@ -70,6 +70,12 @@ constexpr int KEEP_PAIRS = 1;
 // 181.6 / 186.1 / 197.5; B=512, k=3, V=129280 plain early exit 134.0 /
 // 128.9 / 130.7 / 131.1 / 131.0.
 constexpr int EXIT_KEEP_PAIRS = 2;
+// The same for the full read with 512-thread groups (two per CU), where the
+// pair of position 1 kept cached costs more than it saves (B=512, k=3,
+// V=129280 bf16, 1 / 2 pairs: 160.0 / 160.5 us; with every draft accepted
+// 169.8 / 178.1, measured while the bonus draw still took two exponentials
+// per logit).
+constexpr int EXIT_KEEP_PAIRS_WIDE_FULL = 1;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -702,11 +708,62 @@ __device__ __forceinline__ TileGeom tile_geom(int nch, int rem) {
     return g;
 }
 
+// Residual weight max(0, p - q) of one row pair, with each normaliser
+// folded into its exponent: p = 2^(t*c - R_t - log2 Z_t).
+struct ResidualW {
+    float c, nt, nd;  // nt = -(R_t + log2 Z_t), nd likewise for the draft row
+    // p, q in [0, 1], so p - q clamped to [0, 1] is max(0, p - q): one
+    // subtraction with the output clamp instead of a subtraction and a max
+    __device__ __forceinline__ float operator()(float t, float d) const {
+        return __builtin_amdgcn_fmed3f(fast_exp2(fmaf(t, c, nt)) - fast_exp2(fmaf(d, c, nd)),
+                                       0.0f, 1.0f);
+    }
+};
+// Either weight, chosen at run time (uniform), so that one copy of the held
+// draw serves both the residual and the bonus token (each copy of a draw
+// over held registers costs registers of its own): pair, max(0, p - q) as
+// ResidualW; otherwise 2^(t*c + nt), as TargetW with nt = -R (the draft
+// side then reads as -inf and is never loaded).  Each gives exactly the
+// value of the weight it stands for.
+struct DrawW {
+    float c, nt, nd;
+    bool pair;
+    __device__ __forceinline__ float operator()(float t, float d) const {
+        const float pt = fast_exp2(fmaf(t, c, nt));
+        return pair ? __builtin_amdgcn_fmed3f(pt - fast_exp2(fmaf(d, c, nd)), 0.0f, 1.0f) : pt;
+    }
+};
+// Unnormalised target weight 2^(t*c - R).
+struct TargetW {
+    float c, nR;
+    __device__ __forceinline__ float operator()(float t, float) const {
+        return fast_exp2(fmaf(t, c, nR));
+    }
+};
+
 template <bool PAIR, typename C, typename Wt>
 __device__ __forceinline__ float chunk_weight_sum(const Wt& wf, const C& t, const C& d) {
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < C::E; ++e) acc += PAIR ? wf(t.get(e), d.get(e)) : wf(t.get(e), 0.0f);
+    return acc;
+}
+// DrawW's mode is the same for the whole block: one branch per chunk, so
+// the bonus draw takes one exponential per logit, not the residual's two
+// (same terms, same order as the generic sum).
+template <bool PAIR, typename C>
+__device__ __forceinline__ float chunk_weight_sum(const DrawW& wf, const C& t, const C& d) {
+    float acc = 0.0f;
+    if (PAIR && wf.pair) {
+#pragma unroll
+        for (int e = 0; e < C::E; ++e)
+            acc += __builtin_amdgcn_fmed3f(fast_exp2(fmaf(t.get(e), wf.c, wf.nt)) -
+                                               fast_exp2(fmaf(d.get(e), wf.c, wf.nd)),
+                                           0.0f, 1.0f);
+    } else {
+#pragma unroll
+        for (int e = 0; e < C::E; ++e) acc += fast_exp2(fmaf(t.get(e), wf.c, wf.nt));
+    }
     return acc;
 }
 
@@ -1083,39 +1140,6 @@ __device__ __forceinline__ int inverse_cdf_held(const char* trow, const char* dr
     return cdf_select<DT, VEC, PAIR, NT>(tr, dr, wf, r, g, total_out, tile_part, tile_excl, sc,
                                          hold);
 }
-
-// Residual weight max(0, p - q) of one row pair, with each normaliser
-// folded into its exponent: p = 2^(t*c - R_t - log2 Z_t).
-struct ResidualW {
-    float c, nt, nd;  // nt = -(R_t + log2 Z_t), nd likewise for the draft row
-    // p, q in [0, 1], so p - q clamped to [0, 1] is max(0, p - q): one
-    // subtraction with the output clamp instead of a subtraction and a max
-    __device__ __forceinline__ float operator()(float t, float d) const {
-        return __builtin_amdgcn_fmed3f(fast_exp2(fmaf(t, c, nt)) - fast_exp2(fmaf(d, c, nd)),
-                                       0.0f, 1.0f);
-    }
-};
-// Either weight, chosen at run time (uniform), so that one copy of the held
-// draw serves both the residual and the bonus token (each copy of a draw
-// over held registers costs registers of its own): pair, max(0, p - q) as
-// ResidualW; otherwise 2^(t*c + nt), as TargetW with nt = -R (the draft
-// side then reads as -inf and is never loaded).  Each gives exactly the
-// value of the weight it stands for.
-struct DrawW {
-    float c, nt, nd;
-    bool pair;
-    __device__ __forceinline__ float operator()(float t, float d) const {
-        const float pt = fast_exp2(fmaf(t, c, nt));
-        return pair ? __builtin_amdgcn_fmed3f(pt - fast_exp2(fmaf(d, c, nd)), 0.0f, 1.0f) : pt;
-    }
-};
-// Unnormalised target weight 2^(t*c - R).
-struct TargetW {
-    float c, nR;
-    __device__ __forceinline__ float operator()(float t, float) const {
-        return fast_exp2(fmaf(t, c, nR));
-    }
-};
 
 // ------------------------------------------------------------------------
 // Finishing a sequence.
@@ -1528,7 +1552,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             const bool tgt = HOLD ? h == 1 : h == 0;
             const Row<DT, VEC> row(stoch_row<DT>(p, sq, tgt ? i : k + 1 + i), V);
             SoftAcc acc;
-            if (i < EXIT_KEEP_PAIRS) {  // uniform
+            if (i < (FULL && NT < 1024 ? EXIT_KEEP_PAIRS_WIDE_FULL : EXIT_KEEP_PAIRS)) {  // uniform
                 if constexpr (HOLD) {
                     if (tgt) stream_softmax_hold<DT, VEC, NT, true, NH>(row, c, acc, hold.t);
                     else stream_softmax_stash<DT, VEC, NT, true>(row, c, acc, hold.stash, hold.lr);
@@ -1592,6 +1616,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             break;
         }
     }
+    a = __builtin_amdgcn_readfirstlane(a);  // block-uniform: scalar from here on
     if (capped) {
         // 0: rejected, drawn by the spread draw kernels; 1: every streamed
         // pair accepted, the rest of the rows still to read; 2: rejected
@@ -2577,6 +2602,11 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         if (!p.dbg)
             return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHXW, false>, p, p.B,
                            NT_SEQ_WIDE, stream);
+        const long long row_bytes = (long long)p.V * elem_bytes<DT>();
+        if (p.B >= kSeqWideOrderMinB && p.B <= kSeqWideHoldMaxB &&
+            row_bytes >= kSeqWideOrderMinRowBytes)
+            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, kSeqWideOrderHeldRounds, true>,
+                           p, p.B, NT_SEQ_WIDE, stream);
         if (p.B > kSeqWideHoldMaxB)
             return launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, 0>, p, p.B, NT_SEQ_WIDE, stream);
         constexpr int NH = kSeqWideHeldRounds;

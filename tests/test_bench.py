@@ -1,4 +1,5 @@
 """Host-side checks of bench.py's bookkeeping (no GPU)."""
+import dataclasses
 import os
 import subprocess
 import sys
@@ -77,7 +78,16 @@ def test_commit_bytes():
 def test_kernel_names_follow_layouts():
     s2, s1 = W.SPECS[2], W.SPECS[1]
     assert bench.kernel_name(s2, "stochastic") == "k_stochastic_seq_exit (full read)"
-    assert bench.kernel_name(W.SPECS[3], "stochastic") == "k_stochastic_seq"
+    # 512-thread groups: position order from 384 sequences on rows of at
+    # least 160000 bytes (B=512, V=129280 bf16), else pair 0 streamed last
+    assert bench.kernel_name(W.SPECS[3], "stochastic") == "k_stochastic_seq_exit (full read)"
+    s3 = W.SPECS[3]
+    assert bench.kernel_name(dataclasses.replace(s3, B=383), "stochastic") == "k_stochastic_seq"
+    assert bench.kernel_name(dataclasses.replace(s3, B=513), "stochastic") == "k_stochastic_seq"
+    assert bench.kernel_name(dataclasses.replace(s3, V=79999), "stochastic") == "k_stochastic_seq"
+    assert bench.kernel_name(dataclasses.replace(s3, V=80000), "stochastic").startswith("k_stochastic_seq_exit")
+    assert bench.kernel_name(dataclasses.replace(s3, V=40000, dtype=W.F32), "stochastic").startswith(
+        "k_stochastic_seq_exit")
     # without diagnostics: the capped early exit for k >= 6 (B=256, k=8), the
     # plain one below (B=512, k=3)
     assert bench.kernel_name(s2, "stochastic", diagnostics=False).startswith(

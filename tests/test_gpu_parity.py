@@ -187,6 +187,13 @@ STOCH_CASES = [
     # element rows
     (256, 5, 4103, W.BF16, 1.0, 0, False, "equal"),
     (224, 6, 50000, W.F32, 0.8, 0, True, "close"),
+    # the full read in position order with 512-thread groups (384 to 512
+    # sequences, rows of at least 160000 bytes): every draft accepted, the
+    # fp32 bound with rejections at both ends, and the largest batch with a
+    # ragged vector tail and padded rows
+    (384, 1, 80000, W.BF16, 1.0, 0, False, "equal"),
+    (400, 2, 40000, W.F32, 0.7, 0, True, "equaloov"),
+    (512, 2, 80021, W.BF16, 1.0, 3, False, "close"),
 ]
 
 
