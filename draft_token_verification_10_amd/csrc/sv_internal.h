@@ -100,8 +100,10 @@ constexpr int kSampleHeldRounds = 16;
 // rounds of the draft row as fit in the LDS left beside the kernel's own
 // (kLdsBytesPerCu per CU).  Rounds held: as many as fit in the 128 VGPRs
 // that four waves per SIMD allow without spilling, except where holding
-// measured no gain (the early exit with 512-thread groups, two or more per
-// CU: 136.8 against 137.5 us on B=512, k=3, V=129280 bf16).
+// measured slower: the early exit with 512-thread groups on short rows
+// (B=300, k=8, V=32000 bf16: 40.2 us without, 48.2 with; B=512, k=8,
+// V=32000: 46.6 against 53.9) or below 384 sequences (B=300, k=3,
+// V=129280: 101.9 against 102.6), and the capped early exit there.
 //
 // With 1024-thread groups (up to 256 sequences) the early exit and the full
 // read are one kernel that streams the pairs in position order, holding
@@ -113,14 +115,17 @@ constexpr int kSampleHeldRounds = 16;
 // accepting every draft (mean 4.0) 185.3 -> 177.4, a quarter (mean 2.0)
 // 185.3 -> 179.5; but drafts rejected almost always at position 0 (mean
 // 0.1) 185.9 -> 189.3, and every draft accepted 179.8 -> 184.8 (a barrier
-// per pair).  With 512-thread groups the full read runs in position order
-// (12 rounds held) only with two groups on most CUs and long rows: from
-// kSeqWideOrderMinB sequences and kSeqWideOrderMinRowBytes per row, where
-// it measured 0.4 us slower to 10 us faster per call than streaming pair 0
-// last (B=384..512, V=80000..129280 bf16 and 64000 fp32; 9 us faster on
-// B=512, k=3, V=129280 bf16), against 3 to 10 us slower on rows of 128 KB
-// or less (B=300, k=8, V=32000; B=512, k=6, V=64000 bf16) and below 384
-// sequences (B=320, k=8, V=128256).
+// per pair).  With 512-thread groups the early exit holds, and the full
+// read runs in position order, only with two groups on most CUs and long
+// rows: from kSeqWideLongMinB sequences and kSeqWideLongMinRowBytes per
+// row (12 rounds held).  There the full read measured 0.4 us slower to 10
+// us faster per call than streaming pair 0 last (B=384..512,
+// V=80000..129280 bf16 and 64000 fp32; 9 us faster on B=512, k=3,
+// V=129280 bf16), against 3 to 10 us slower on rows of 128 KB or less
+// (B=300, k=8, V=32000; B=512, k=6, V=64000 bf16) and below 384 sequences
+// (B=320, k=8, V=128256); the early exit 130.1 -> 125.0 us on B=512, k=3,
+// V=129280 (with every draft accepted, V=128256: 170.5 -> 156.9; half the
+// sequences: 141.1 -> 131.9), within 1 us either way from 384 to 448.
 #ifndef SV_HOLD_SEQ_512
 #define SV_HOLD_SEQ_512 16
 #endif
@@ -137,12 +142,12 @@ constexpr int kPairHeldRounds = 16;  // the most any kernel holds
 // nothing is held there (B=700, k=8, V=32000 bf16: 132.6 us without, 161.1
 // with; B=1024, k=3, V=128256: 339.4 without, 334.5 with, two full rounds).
 constexpr int kSeqWideHoldMaxB = 512;
-constexpr int kSeqWideOrderMinB = 384;
-constexpr long long kSeqWideOrderMinRowBytes = 160000;
-#ifndef SV_HOLD_FULL_512
-#define SV_HOLD_FULL_512 12
+constexpr int kSeqWideLongMinB = 384;
+constexpr long long kSeqWideLongMinRowBytes = 160000;
+#ifndef SV_HOLD_LONG_512
+#define SV_HOLD_LONG_512 12
 #endif
-constexpr int kSeqWideOrderHeldRounds = SV_HOLD_FULL_512;
+constexpr int kSeqWideLongHeldRounds = SV_HOLD_LONG_512;
 constexpr int kSeqWideHeldRounds = SV_HOLD_SEQ_512;  // full read, 512-thread groups
 constexpr int held_rounds_exit(int nt) { return nt >= 1024 ? SV_HOLD_EXIT_1024 : SV_HOLD_EXIT_512; }
 constexpr size_t kLdsBytesPerCu = 160 * 1024;

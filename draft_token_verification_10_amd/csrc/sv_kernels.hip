@@ -70,12 +70,13 @@ constexpr int KEEP_PAIRS = 1;
 // 181.6 / 186.1 / 197.5; B=512, k=3, V=129280 plain early exit 134.0 /
 // 128.9 / 130.7 / 131.1 / 131.0.
 constexpr int EXIT_KEEP_PAIRS = 2;
-// The same for the full read with 512-thread groups (two per CU), where the
-// pair of position 1 kept cached costs more than it saves (B=512, k=3,
-// V=129280 bf16, 1 / 2 pairs: 160.0 / 160.5 us; with every draft accepted
-// 169.8 / 178.1, measured while the bonus draw still took two exponentials
-// per logit).
-constexpr int EXIT_KEEP_PAIRS_WIDE_FULL = 1;
+// The same for 512-thread groups (two per CU) that hold the pair on chip,
+// where the pair of position 1 kept cached costs more than it saves: full
+// read, B=512, k=3, V=129280 bf16, 1 / 2 pairs: 160.0 / 160.5 us (with
+// every draft accepted 169.8 / 178.1, measured while the bonus draw still
+// took two exponentials per logit); early exit 125.0 / 126.6, with every
+// draft accepted (V=128256) 156.9 / 169.8.
+constexpr int EXIT_KEEP_PAIRS_WIDE_HELD = 1;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -1552,7 +1553,7 @@ __global__ __launch_bounds__(NT) void k_stochastic_seq_exit(Params p) {
             const bool tgt = HOLD ? h == 1 : h == 0;
             const Row<DT, VEC> row(stoch_row<DT>(p, sq, tgt ? i : k + 1 + i), V);
             SoftAcc acc;
-            if (i < (FULL && NT < 1024 ? EXIT_KEEP_PAIRS_WIDE_FULL : EXIT_KEEP_PAIRS)) {  // uniform
+            if (i < (HOLD && NT < 1024 ? EXIT_KEEP_PAIRS_WIDE_HELD : EXIT_KEEP_PAIRS)) {  // uniform
                 if constexpr (HOLD) {
                     if (tgt) stream_softmax_hold<DT, VEC, NT, true, NH>(row, c, acc, hold.t);
                     else stream_softmax_stash<DT, VEC, NT, true>(row, c, acc, hold.stash, hold.lr);
@@ -2599,14 +2600,20 @@ static int launch_stochastic_t(const Params& p, bool seq, void* stream) {
         return launch1(k_draw_tiles<DT, VEC>, p, (long long)p.B * p.SD, NT_DRAW, stream);
     }
     if (seq && p.B >= kSeqWideMinB) {
-        if (!p.dbg)
-            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHXW, false>, p, p.B,
-                           NT_SEQ_WIDE, stream);
+        // long rows, two groups on most CUs: the pair streamed last held on
+        // chip, in the early exit and in the full read in position order
+        constexpr int NHL = kSeqWideLongHeldRounds;
         const long long row_bytes = (long long)p.V * elem_bytes<DT>();
-        if (p.B >= kSeqWideOrderMinB && p.B <= kSeqWideHoldMaxB &&
-            row_bytes >= kSeqWideOrderMinRowBytes)
-            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, kSeqWideOrderHeldRounds, true>,
-                           p, p.B, NT_SEQ_WIDE, stream);
+        const bool held = p.B >= kSeqWideLongMinB && p.B <= kSeqWideHoldMaxB &&
+                          row_bytes >= kSeqWideLongMinRowBytes;
+        if (!p.dbg)
+            return held ? launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHL, false>, p, p.B,
+                                  NT_SEQ_WIDE, stream)
+                        : launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHXW, false>, p, p.B,
+                                  NT_SEQ_WIDE, stream);
+        if (held)
+            return launch1(k_stochastic_seq_exit<DT, VEC, NT_SEQ_WIDE, NHL, true>, p, p.B,
+                           NT_SEQ_WIDE, stream);
         if (p.B > kSeqWideHoldMaxB)
             return launch1(k_stochastic_seq<DT, VEC, NT_SEQ_WIDE, 0>, p, p.B, NT_SEQ_WIDE, stream);
         constexpr int NH = kSeqWideHeldRounds;

@@ -480,15 +480,17 @@ def test_ragged_no_drafts(B):
     assert np.all(a == 0)
 
 
-@pytest.mark.parametrize("B", [4, 256])
-def test_ragged_uniform_matches_dense(B):
+# the last: 512-thread groups in position order (long rows, B >= 384)
+@pytest.mark.parametrize("B,V,dtype", [(4, 4103, W.BF16), (256, 4103, W.BF16),
+                                       (400, 40000, W.F32)])
+def test_ragged_uniform_matches_dense(B, V, dtype):
     """Every k_b = k: the ragged call returns exactly what the dense call does."""
-    print(f"ragged uniform B={B}", flush=True)
-    k, V = 5, 4103
-    t, d, x, ua, us = make_stochastic(B + 77, B, k, V, W.BF16, 1.0)
+    print(f"ragged uniform B={B} V={V}", flush=True)
+    k = 5
+    t, d, x, ua, us = make_stochastic(B + 77, B, k, V, dtype, 1.0)
     cu = (np.arange(B + 1) * k).astype(np.int32)
-    tt, _, _ = logits_to_device(t, W.BF16)
-    dt, _, _ = logits_to_device(d, W.BF16)
+    tt, _, _ = logits_to_device(t, dtype)
+    dt, _, _ = logits_to_device(d, dtype)
     args = [dev(x.reshape(-1)), dev(cu), dev(ua.reshape(-1)), dev(us)]
     dbg_r = torch.empty((B * k, 2), dtype=torch.float32, device=DEV)
     dbg_d = torch.empty((B, k, 2), dtype=torch.float32, device=DEV)
