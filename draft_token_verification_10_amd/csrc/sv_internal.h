@@ -148,7 +148,7 @@ constexpr long long kSeqWideLongMinRowBytes = 160000;
 #define SV_HOLD_LONG_512 12
 #endif
 constexpr int kSeqWideLongHeldRounds = SV_HOLD_LONG_512;
-constexpr int kSeqWideHeldRounds = SV_HOLD_SEQ_512;  // full read, 512-thread groups
+constexpr int kSeqWideHeldRounds = SV_HOLD_SEQ_512;  // full read with pair 0 last, 512 threads
 constexpr int held_rounds_exit(int nt) { return nt >= 1024 ? SV_HOLD_EXIT_1024 : SV_HOLD_EXIT_512; }
 constexpr size_t kLdsBytesPerCu = 160 * 1024;
 constexpr long long kSampleSeqBaseElems = 40960;

@@ -1403,8 +1403,9 @@ struct StochSeqSmem : StochSeqBase<NT> {
     uint4 stash[LR > 0 ? LR * NT : 1];
 };
 
-// The full read with 512-thread groups (more sequences than CUs; up to 256
-// sequences the full read runs in position order in k_stochastic_seq_exit).
+// The full read with 512-thread groups (more sequences than CUs), except
+// on long rows from 384 to 512 sequences; up to 256 sequences, and there,
+// the full read runs in position order in k_stochastic_seq_exit.
 // NH: target rounds of pair 0 held in registers (0: nothing held, which
 // leaves room for more workgroups per CU).
 template <int DT, bool VEC, int NT, int NH>
