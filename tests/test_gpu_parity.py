@@ -194,6 +194,10 @@ STOCH_CASES = [
     (384, 1, 80000, W.BF16, 1.0, 0, False, "equal"),
     (400, 2, 40000, W.F32, 0.7, 0, True, "equaloov"),
     (512, 2, 80021, W.BF16, 1.0, 3, False, "close"),
+    # just outside that layout: pair 0 streamed last (383 sequences), and
+    # nothing held (513)
+    (383, 2, 80000, W.BF16, 1.0, 0, False, "equaloov"),
+    (513, 1, 40000, W.F32, 0.7, 0, True, None),
 ]
 
 
