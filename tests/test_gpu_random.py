@@ -70,7 +70,29 @@ def small_batch_cases(n=40, seed=37):
     return cases
 
 
-@pytest.mark.parametrize("case", random_cases() + small_batch_cases(),
+def wide_long_cases(n=8, seed=41):
+    """384 to 512 sequences on rows of at least 160000 bytes: 512-thread
+    groups holding the pair streamed last (the early exit, and the full read
+    in position order), and ragged batches of uniform length there."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        mode = ["stochastic", "stochastic", "ragged", "stochastic"][len(cases) % 4]
+        B = int(rng.integers(384, 513))
+        dtype = int(rng.choice([W.F32, W.BF16]))
+        s = 2 if dtype == W.BF16 else 4
+        V = int(rng.integers(-(-160000 // s), 140_001))
+        k = int(rng.integers(1, 4))
+        tau = float(rng.choice([0.7, 1.0]))
+        pad = int(rng.integers(1, 9)) if rng.random() < 0.25 else 0
+        unal = bool(rng.random() < 0.25)
+        if B * (2 * k + 1) * (V + pad) > 250_000_000:
+            continue
+        cases.append((2000 + len(cases), mode, B, 1, k, V, dtype, tau, pad, unal))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_cases() + small_batch_cases() + wide_long_cases(),
                          ids=lambda c: "{}_{}_B{}_G{}_k{}_V{}_{}_t{}_p{}_u{}".format(
     c[0], c[1], c[2], c[3], c[4], c[5], "bf16" if c[6] else "f32", c[7], c[8], int(c[9])))
 def test_random_shape(case):
