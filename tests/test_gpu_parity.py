@@ -475,11 +475,12 @@ def test_ragged(case):
     assert rep.ok(), rep.summary()
 
 
-@pytest.mark.parametrize("B", [6, 200])
-def test_ragged_no_drafts(B):
-    """Every k_b = 0: the call samples each sequence's one target row."""
-    print(f"ragged no drafts B={B}", flush=True)
-    cu, t, d, x, ua, us = make_ragged(B, B, 4, 3001, W.BF16, 1.0, kb=np.zeros(B))
+@pytest.mark.parametrize("B,V", [(6, 3001), (200, 3001), (400, 80000)])
+def test_ragged_no_drafts(B, V):
+    """Every k_b = 0: the call samples each sequence's one target row (the
+    last case in 512-thread groups holding the row on chip)."""
+    print(f"ragged no drafts B={B} V={V}", flush=True)
+    cu, t, d, x, ua, us = make_ragged(B, B, 4, V, W.BF16, 1.0, kb=np.zeros(B))
     rep, a = run_ragged(cu, t, d, x, ua, us, 4, 1.0, W.BF16)
     assert rep.ok(), rep.summary()
     assert np.all(a == 0)
